@@ -1,0 +1,409 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+Each test checks the oracle against something the pages or the mathematics fix:
+textbook dense attention done with library routines, brute force on tiny
+inputs, closed forms, exact invariances, hand-derived fixtures and the live
+shapes that page 2 prints.  Together they are chosen so that a plausible slip
+in the oracle (a dropped RoPE term, V taken from the wrong dims, the mask
+transposed or with the prefix-only stride, a missing scale, a log2 LSE, a
+wrong head/draft mapping, kv_indices ignored, indptr offsets ignored) fails
+at least one of them.  No GPU needed.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+import oracle
+import tv_workload as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f64(bits):
+    return W.bf16_to_f32(bits).astype(np.float64)
+
+
+def textbook(w, b, rows_tok, keys_j):
+    """Dense softmax(c * Q K^T) V over an explicit key list, via scipy/numpy."""
+    k0 = int(w.kv_indptr[b])
+    K = f64(w.kv[w.kv_indices[k0 + np.asarray(keys_j)]])
+    Q = f64(w.q[rows_tok])  # [n, H, 576]
+    c = float(w.sm_scale)
+    S = c * np.einsum("nhd,kd->nhk", Q, K)
+    P = softmax(S, axis=-1)
+    return P @ K[:, :512], logsumexp(S, axis=-1)
+
+
+def dense_all_visible(w):
+    w.mask[:] = 1
+    return w
+
+
+# ---------------------------------------------------------------- I1 dense case
+
+@pytest.mark.parametrize("outlier_p", [0.0, 0.01])
+def test_dense_mask_equals_textbook_attention(outlier_p):
+    w = dense_all_visible(W.small(11, [37, 5], [4, 3], num_heads=3, outlier_p=outlier_p))
+    o, l = oracle.run(w)
+    for b in range(w.batch):
+        toks = np.arange(w.qo_indptr[b], w.qo_indptr[b + 1])
+        L = int(w.kv_lens[b])
+        ro, rl = textbook(w, b, toks, np.arange(L))
+        np.testing.assert_allclose(o[toks], ro, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l[toks], rl, rtol=1e-13, atol=1e-13)
+
+
+def test_duplicate_slots_are_separate_keys():
+    w = dense_all_visible(W.small(12, [6], [2], num_heads=2))
+    w.kv_indices[1] = w.kv_indices[0]   # same slot gathered twice
+    w.kv_indices[3] = w.kv_indices[0]
+    o, l = oracle.run(w)
+    ro, rl = textbook(w, 0, np.arange(2), np.arange(int(w.kv_lens[0])))
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l, rl, rtol=1e-13)
+
+
+# ---------------------------------------------------------- I2 ancestor subset
+
+def test_tree_row_equals_attention_over_its_path():
+    w = W.small(13, [23], [9], num_heads=4)
+    o, l = oracle.run(w)
+    P = w.prefix_lens[0]
+    for i in range(9):
+        path = W.ancestors_and_self(w.parents[0], i)
+        keys = list(range(P)) + [P + k for k in path]
+        # same keys in the same ascending order, as a one-row dense request
+        sub = W.Workload(q=w.q[i:i + 1], kv=w.kv, kv_indices=w.kv_indices[keys],
+                         kv_indptr=np.array([0, len(keys)], np.int32),
+                         qo_indptr=np.array([0, 1], np.int32),
+                         mask=np.ones(len(keys), np.uint8),
+                         mask_indptr=np.array([0, len(keys)], np.int32),
+                         sm_scale=w.sm_scale, num_heads=4)
+        so, sl = oracle.run(sub)
+        assert np.array_equal(so[0], o[i]) and np.array_equal(sl[0], l[i])
+
+
+# --------------------------------------------------------- I3 slot permutation
+
+def test_slot_permutation_is_bit_identical():
+    w = W.small(14, [40, 17], [6, 4], num_heads=2)
+    o, l = oracle.run(w)
+    rng = np.random.default_rng(0)
+    pi = rng.permutation(w.num_slots)
+    kv2 = np.empty_like(w.kv)
+    kv2[pi] = w.kv                      # row s moves to pi[s]
+    w2 = W.Workload(**{**w.__dict__, "kv": kv2, "kv_indices": pi[w.kv_indices].astype(np.int32)})
+    o2, l2 = oracle.run(w2)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+# ----------------------------------------------------------------- I4 one key
+
+def test_single_visible_key_returns_its_value():
+    w = W.small(15, [8], [3], num_heads=2)
+    w.mask[:] = 0
+    L = int(w.kv_lens[0])
+    picks = [0, 5, L - 1]
+    for i, j in enumerate(picks):
+        w.mask[i * L + j] = 1
+    o, l = oracle.run(w)
+    for i, j in enumerate(picks):
+        k = f64(w.kv[w.kv_indices[j]])
+        for h in range(2):
+            assert np.array_equal(o[i, h], k[:512])
+            s = float(w.sm_scale) * math.fsum(f64(w.q[i, h]) * k)
+            assert abs(l[i, h] - s) <= 1e-13 * max(1.0, abs(s))
+
+
+# ---------------------------------------------------------- I5 brute force
+
+def brute(w):
+    """Scalar loops, math.fsum, exp(s)/sum(exp(s)) with no max shift."""
+    N, H = w.q.shape[0], w.num_heads
+    out = np.zeros((N, H, 512))
+    lse = np.full((N, H), -np.inf)
+    c = float(w.sm_scale)
+    for b in range(w.batch):
+        n = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        L = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        for i in range(n):
+            t = int(w.qo_indptr[b]) + i
+            vis = [j for j in range(L) if w.mask[int(w.mask_indptr[b]) + i * L + j]]
+            for h in range(H):
+                if not vis:
+                    continue
+                qv = [float(x) for x in f64(w.q[t, h])]
+                ks = [[float(x) for x in f64(w.kv[w.kv_indices[int(w.kv_indptr[b]) + j]])]
+                      for j in vis]
+                e = [math.exp(c * math.fsum(a * bb for a, bb in zip(qv, k))) for k in ks]
+                z = math.fsum(e)
+                for d in range(512):
+                    out[t, h, d] = math.fsum(e[v] * ks[v][d] for v in range(len(vis))) / z
+                lse[t, h] = math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H", [(21, [3], [3], 2), (22, [2, 3], [2, 3], 1),
+                                                   (23, [0, 1], [3, 2], 2)])
+def test_brute_force_tiny(seed, prefix, ndraft, H):
+    w = W.small(seed, prefix, ndraft, num_heads=H)
+    # random (not tree) visibility so off-path entries matter too; keep >= 1 visible per row
+    rng = np.random.default_rng(seed)
+    w.mask[:] = (rng.random(w.mask.size) < 0.6).astype(np.uint8)
+    o, l = oracle.run(w)
+    bo, bl = brute(w)
+    np.testing.assert_allclose(o, bo, rtol=1e-13, atol=1e-13)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(l))
+    np.testing.assert_allclose(l[fin], bl[fin], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------ I6 q = 0
+
+def test_zero_query_gives_mean_of_visible_values():
+    w = W.small(16, [29, 7], [5, 4], num_heads=3)
+    w.q[:] = 0
+    o, l = oracle.run(w)
+    for b in range(w.batch):
+        L = int(w.kv_lens[b])
+        for i in range(int(w.q_lens[b])):
+            t = int(w.qo_indptr[b]) + i
+            row = w.mask[int(w.mask_indptr[b]) + i * L: int(w.mask_indptr[b]) + (i + 1) * L]
+            vis = np.flatnonzero(row)
+            V = f64(w.kv[w.kv_indices[int(w.kv_indptr[b]) + vis]])[:, :512]
+            mean = np.array([math.fsum(V[:, d]) for d in range(512)]) / len(vis)
+            for h in range(3):
+                np.testing.assert_allclose(o[t, h], mean, rtol=1e-15, atol=1e-15)
+                assert abs(l[t, h] - math.log(len(vis))) <= 1e-15 * max(1, math.log(len(vis)))
+
+
+def test_hand_derived_fixture():
+    g = json.load(open(os.path.join(GOLD, "closed_form_tiny.json")))
+    kvf = np.zeros((g["num_slots"], 576), np.float32)
+    for j, s in enumerate(g["kv_indices"]):
+        kvf[s, 0] = g["key_dim0"][j]
+        kvf[s, 1] = g["key_dim1"][j]
+        kvf[s, 511] = g["key_dim511"][j]
+        kvf[s, 512] = g["key_dim512"][j]
+    n = len(g["parent"])
+    L = g["prefix_len"] + n
+    mask = np.array(g["mask"], np.uint8)
+    assert mask.size == n * L
+    o, l = oracle.attention(np.zeros((n, 1, 576), np.uint16), W.bf16_round(kvf),
+                            np.array(g["kv_indices"]), np.array(g["kv_indptr"]),
+                            np.array(g["qo_indptr"]), mask, np.array(g["mask_indptr"]),
+                            W.SM_SCALE, 1)
+    for i in range(n):
+        e = g["expected"]["row%d" % i]
+        ref = np.zeros(512)
+        ref[0], ref[1], ref[511] = e["dim0"], e["dim1"], e["dim511"]
+        assert np.array_equal(o[i, 0], ref)
+        assert abs(l[i, 0] - e["lse"]) < 1e-15
+
+
+# ------------------------------------------------------ I7 two visible keys
+
+def test_two_visible_keys_closed_form():
+    w = W.small(17, [10], [2], num_heads=2)
+    w.mask[:] = 0
+    L = int(w.kv_lens[0])
+    pairs = [(1, 7), (0, L - 1)]
+    for i, (a, b) in enumerate(pairs):
+        w.mask[i * L + a] = w.mask[i * L + b] = 1
+    o, l = oracle.run(w)
+    c = float(w.sm_scale)
+    for i, (a, b) in enumerate(pairs):
+        ka, kb = f64(w.kv[w.kv_indices[a]]), f64(w.kv[w.kv_indices[b]])
+        for h in range(2):
+            qv = f64(w.q[i, h])
+            sa, sb = c * math.fsum(qv * ka), c * math.fsum(qv * kb)
+            wa = 1.0 / (1.0 + math.exp(sb - sa))
+            wb = 1.0 / (1.0 + math.exp(sa - sb))
+            np.testing.assert_allclose(o[i, h], wa * ka[:512] + wb * kb[:512], rtol=1e-14, atol=1e-14)
+            ref_l = max(sa, sb) + math.log1p(math.exp(-abs(sa - sb)))
+            assert abs(l[i, h] - ref_l) <= 1e-14 * max(1.0, abs(ref_l))
+
+
+# -------------------------------------------------------- I8 merge identity
+
+def test_disjoint_key_sets_merge_by_lse():
+    """Attention over A u B from the two halves: the identity a KV split relies on."""
+    w = W.small(18, [50], [4], num_heads=2)
+    o, l = oracle.run(w)
+    L = int(w.kv_lens[0])
+    cut = 23
+    wa = W.Workload(**{**w.__dict__, "mask": w.mask.copy()})
+    wb = W.Workload(**{**w.__dict__, "mask": w.mask.copy()})
+    for i in range(4):
+        wa.mask[i * L + cut:(i + 1) * L] = 0
+        wb.mask[i * L:i * L + cut] = 0
+    oa, la = oracle.run(wa)
+    ob, lb = oracle.run(wb)
+    lm = np.logaddexp(la, lb)
+    om = np.exp(la - lm)[..., None] * oa + np.exp(lb - lm)[..., None] * ob
+    np.testing.assert_allclose(lm, l, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(om, o, rtol=1e-13, atol=1e-13)
+
+
+# ----------------------------------------------- I9 / I10 relabelings
+
+def test_head_permutation_permutes_outputs():
+    w = W.small(19, [31], [5], num_heads=5)
+    o, l = oracle.run(w)
+    perm = np.array([3, 0, 4, 1, 2])
+    w2 = W.Workload(**{**w.__dict__, "q": np.ascontiguousarray(w.q[:, perm])})
+    o2, l2 = oracle.run(w2)
+    assert np.array_equal(o2, o[:, perm]) and np.array_equal(l2, l[:, perm])
+
+
+def test_draft_row_permutation_permutes_outputs():
+    w = W.small(20, [12], [6], num_heads=2)
+    o, l = oracle.run(w)
+    L = int(w.kv_lens[0])
+    perm = np.array([5, 2, 0, 4, 1, 3])
+    m = w.mask.reshape(6, L)[perm].reshape(-1)
+    w2 = W.Workload(**{**w.__dict__, "q": np.ascontiguousarray(w.q[perm]), "mask": m})
+    o2, l2 = oracle.run(w2)
+    assert np.array_equal(o2, o[perm]) and np.array_equal(l2, l[perm])
+
+
+def test_draft_relabeling_with_key_columns():
+    """Relabel the drafts: q rows, mask rows and columns and draft slots move together."""
+    w = W.small(24, [9], [5], num_heads=2)
+    o, l = oracle.run(w)
+    P, n = w.prefix_lens[0], 5
+    L = P + n
+    perm = np.array([2, 4, 0, 3, 1])  # new draft a is old draft perm[a]
+    m = w.mask.reshape(n, L)
+    cols = np.concatenate([np.arange(P), P + perm])
+    m2 = m[perm][:, cols].reshape(-1)
+    ki = w.kv_indices.copy()
+    ki[P:] = w.kv_indices[P + perm]
+    w2 = W.Workload(**{**w.__dict__, "q": np.ascontiguousarray(w.q[perm]), "mask": m2,
+                       "kv_indices": ki})
+    o2, l2 = oracle.run(w2)
+    np.testing.assert_allclose(o2, o[perm], rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(l2, l[perm], rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------- batch structure and offsets
+
+def test_batch_equals_requests_run_alone():
+    w = W.small(25, [13, 0, 40, 5], [3, 2, 4, 1], num_heads=2)
+    o, l = oracle.run(w)
+    for b in range(w.batch):
+        q0, q1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        k0, k1 = int(w.kv_indptr[b]), int(w.kv_indptr[b + 1])
+        m0, m1 = int(w.mask_indptr[b]), int(w.mask_indptr[b + 1])
+        sub = W.Workload(q=w.q[q0:q1], kv=w.kv, kv_indices=w.kv_indices[k0:k1],
+                         kv_indptr=np.array([0, k1 - k0], np.int32),
+                         qo_indptr=np.array([0, q1 - q0], np.int32), mask=w.mask[m0:m1],
+                         mask_indptr=np.array([0, m1 - m0], np.int32), sm_scale=w.sm_scale,
+                         num_heads=2)
+        so, sl = oracle.run(sub)
+        assert np.array_equal(so, o[q0:q1]) and np.array_equal(sl, l[q0:q1])
+
+
+def test_indptr_offsets_are_honoured():
+    w = W.small(26, [7, 19], [3, 2], num_heads=2)
+    o, l = oracle.run(w)
+    pad_k, pad_m = 11, 29
+    ki = np.concatenate([np.zeros(pad_k, np.int32), w.kv_indices])
+    mk = np.concatenate([np.full(pad_m, 1, np.uint8), w.mask])
+    w2 = W.Workload(**{**w.__dict__, "kv_indices": ki, "mask": mk,
+                       "kv_indptr": (w.kv_indptr + pad_k).astype(np.int32),
+                       "mask_indptr": (w.mask_indptr + pad_m).astype(np.int32)})
+    o2, l2 = oracle.run(w2)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+def test_row_subset_matches_full_run():
+    w = W.small(27, [33, 4], [4, 5], num_heads=3)
+    o, l = oracle.run(w)
+    rows = np.array([0, 5, 13, 26, 9])
+    so, sl = oracle.run(w, rows=rows)
+    H = 3
+    for r, g in enumerate(rows):
+        assert np.array_equal(so[r], o[g // H, g % H]) and sl[r] == l[g // H, g % H]
+
+
+# ---------------------------------------------------------- degenerate cases
+
+def test_row_with_no_visible_key():
+    w = W.small(28, [6], [3], num_heads=2)
+    L = int(w.kv_lens[0])
+    w.mask[L:2 * L] = 0
+    o, l = oracle.run(w)
+    assert np.all(o[1] == 0) and np.all(l[1] == -np.inf)
+    assert np.all(np.isfinite(l[[0, 2]]))
+
+
+def test_empty_batch_and_empty_request():
+    w = W.small(29, [5, 3], [0, 2], num_heads=1)
+    o, l = oracle.run(w)
+    assert o.shape == (2, 1, 512) and np.all(np.isfinite(l))
+
+
+def test_poisoned_pool_rows_are_never_read():
+    w = W.small(30, [20], [4], num_heads=2, poison=True)
+    assert np.isnan(f64(w.kv)).any(axis=1).sum() > 0
+    o, l = oracle.run(w)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ---------------------------------------------- preconditions / pages' bug
+
+def test_live_shapes_fix_the_mask_stride():
+    g = json.load(open(os.path.join(GOLD, "live_shapes.json")))
+    n, P = g["n_draft"], g["prefix_len"]
+    assert g["mask"][0] == n * (P + n)
+    w = W.config(1)
+    assert list(w.q.shape) == g["q"] and w.num_heads == g["num_heads_per_rank"]
+    assert w.mask.size == g["mask"][0] and int(w.kv_lens[0]) == P + n
+
+
+def test_marshaling_bug_is_rejected():
+    """Both halves of the pages' marshaling bug violate the precondition."""
+    w = W.config(1)
+    P, n = 21, 9
+    assert oracle.check_workload(w) == 0
+    # draft slots missing from kv_indices, mask still at the full stride
+    w1 = W.Workload(**{**w.__dict__, "kv_indices": w.kv_indices[:P],
+                       "kv_indptr": np.array([0, P], np.int32)})
+    assert oracle.check_workload(w1) == -5
+    # draft slots present, mask laid out with the prefix-only stride
+    m = w.mask.reshape(n, P + n)[:, :P].reshape(-1)
+    w2 = W.Workload(**{**w.__dict__, "mask": m, "mask_indptr": np.array([0, n * P], np.int32)})
+    assert oracle.check_workload(w2) == -5
+    with pytest.raises(oracle.OracleError):
+        oracle.run(w2)
+
+
+def test_other_preconditions():
+    w = W.small(31, [5], [3], num_heads=1)
+    bad = W.Workload(**{**w.__dict__, "kv_indices": w.kv_indices.copy()})
+    bad.kv_indices[2] = w.num_slots
+    assert oracle.check_workload(bad) == -6
+    bad2 = W.Workload(**{**w.__dict__, "kv_indptr": np.array([0, 2], np.int32),
+                         "mask_indptr": np.array([0, 6], np.int32)})
+    assert oracle.check_workload(bad2) == -4
+    bad3 = W.Workload(**{**w.__dict__, "qo_indptr": np.array([2, 1], np.int32)})
+    assert oracle.check_workload(bad3) == -3
+
+
+# ------------------------------------------------- generator structure
+
+def test_generated_configs_structure():
+    for k in (1, 2):
+        w = W.config(k)
+        assert oracle.check_workload(w) == 0
+        for b in range(w.batch):
+            L, n, P = int(w.kv_lens[b]), int(w.q_lens[b]), w.prefix_lens[b]
+            m = w.mask[int(w.mask_indptr[b]):int(w.mask_indptr[b + 1])].reshape(n, L)
+            assert np.all(m[:, :P] == 1)
+            assert np.all(np.diag(m[:, P:]) == 1)          # each draft sees itself
+            assert np.all(np.triu(m[:, P:], 1) == 0)        # never a later draft
