@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of tree-masked verify attention on one MI355X.
+
+One step = one tv_verify_attn call (mask packing + split attention + LSE merge)
+over one batch of seeded synthetic inputs already resident in HBM, replayed from
+a captured HIP graph.  Default workload: 1 request, 32 draft tokens, 32768-key
+prefix, 16 heads (the 32k-prefix configuration the metric is quoted at).
+
+Prints one JSON line: throughput as gathered-KV GB/s (sum over requests of
+L_b * 1152 bytes per call / call time), the roofline of the split kernel timed
+live with HIP events, and the fp64 CPU oracle timed on a bounded sample.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tv_workload as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (torch's events cannot be handed to the C ABI)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return e.value
+
+    def record(self, ev: int, stream: int):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self.lib.hipEventSynchronize(ctypes.c_void_p(b))
+        f = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(f.value)
+
+    def destroy(self, ev: int):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def workload(cfg: str, poison: bool):
+    if cfg.startswith("S"):
+        k = int(cfg[1:])
+        w = W.sweep(k, poison=poison)
+        desc = "S%d: 1 request, n_draft=9, prefix %d, H=8 (live shape at long prefix)" % (
+            k, W.SWEEP_PREFIX[k])
+        return w, desc, None
+    k = int(cfg)
+    return W.config(k, poison=poison), W.CONFIG_DESC[k], W.CONFIG_SPLITS.get(k)
+
+
+def algorithmic(w):
+    """Bytes the call must move and flops it must do (visible pairs only)."""
+    H = w.num_heads
+    kv_bytes = w.gathered_kv_bytes()
+    nq = w.total_q
+    total_bytes = (kv_bytes + nq * H * 576 * 2 + nq * H * 512 * 2 + nq * H * 4 +
+                   int(w.kv_lens.sum()) * 4 + int(w.mask.size))
+    flops = 2.0 * (576 + 512) * H * w.visible_pairs()
+    return kv_bytes, total_bytes, flops
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("tv_kernels.hip", "tv_kernels.h", "tv_api.cpp"):
+        h.update(open(os.path.join(ROOT, "tree_verify_mla_paged_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: str, splits):
+    """HBM bytes per split-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "split_kernel_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    e = d.get("workloads", {}).get(str(cfg))
+    if not e or e.get("source_hash") != source_hash() or e.get("splits") != splits:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, gpu_out, gpu_lse, kv_bytes, budget_s, out_f32):
+    """Time the fp64 oracle on a bounded sample of rows and scale to the call."""
+    import oracle
+    H = w.num_heads
+    total_rows = w.total_q * H
+    threads = os.cpu_count() or 1
+    rng = np.random.default_rng(123)
+    order = rng.permutation(total_rows)
+    # probe a few rows to size the sample for the time budget
+    probe = np.sort(order[:min(total_rows, max(4, threads))])
+    t0 = time.perf_counter()
+    oracle.run(w, rows=probe, threads=threads)
+    t_probe = time.perf_counter() - t0
+    per_row = t_probe / len(probe)
+    n = int(min(total_rows, max(len(probe), budget_s / max(per_row, 1e-9))))
+    rows = np.sort(order[:n])
+    t0 = time.perf_counter()
+    ro, rl = oracle.run(w, rows=rows, threads=threads)
+    t = time.perf_counter() - t0
+    # the sampled rows see this share of the call's (row, key) pairs
+    lens = np.repeat(w.kv_lens, w.q_lens * H).astype(np.float64)
+    share = lens[rows].sum() / max(lens.sum(), 1.0)
+    t_call = t / max(share, 1e-12)
+    go = gpu_out.reshape(-1, 512)[rows]
+    gl = gpu_lse.reshape(-1)[rows]
+    d = np.abs(go - ro)
+    fin = np.isfinite(rl)
+    parity = {
+        "rows": int(n), "max_abs_diff": float(d.max()),
+        "mean_rel_err": float(d.sum() / max(np.abs(ro).sum(), 1e-300)),
+        "max_lse_diff": float(np.abs(gl[fin] - rl[fin]).max()) if fin.any() else 0.0,
+        "out_dtype": "f32" if out_f32 else "bf16",
+    }
+    return {
+        "value": kv_bytes / t_call / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "%d of %d rows (%.1f%% of row-key pairs), fp64 C/OpenMP, %.2f s measured, "
+                  "%.2f s per full call" % (n, total_rows, 100 * share, t, t_call),
+        "us_per_call": t_call * 1e6, "parity_vs_gpu": parity,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="3", help="1-5 (benchmark configurations) or S1-S3")
+    ap.add_argument("--splits", type=int, default=-1,
+                    help="KV split count (0 = library heuristic; default: the configuration's own "
+                         "split count if it names one, else the heuristic)")
+    ap.add_argument("--out-f32", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requests and heads "
+              "shard with no exchange; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tree_verify_mla_paged_amd as tv
+
+    w, desc, cfg_splits = workload(args.config, poison=False)
+    splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
+    dev = "cuda"
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in dict(
+        q=w.q.view(np.int16), kv=w.kv.view(np.int16), kv_indices=w.kv_indices,
+        kv_indptr=w.kv_indptr, qo_indptr=w.qo_indptr, mask=w.mask,
+        mask_indptr=w.mask_indptr).items()}
+    p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
+                        int(w.kv_indices.size), int(w.mask.size), splits,
+                        tv.OUT_F32 if args.out_f32 else tv.OUT_BF16)
+    plan = tv.plan(p)
+    N, H = w.total_q, w.num_heads
+    out = torch.empty((N, H, 512), dtype=torch.float32 if args.out_f32 else torch.bfloat16,
+                      device=dev)
+    lse = torch.empty((N, H), dtype=torch.float32, device=dev)
+    nb = tv.workspace_bytes(p)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    sid = int(stream.cuda_stream)
+
+    def call():
+        tv.verify_attn(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                       t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws, ws.numel(),
+                       stream=sid)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` graph replays
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # the split kernel alone, timed with HIP events on its own stream
+    ev = HipEvents()
+    nrep = max(20, min(args.steps, 200))
+    pairs = [(ev.create(), ev.create()) for _ in range(nrep)]
+    whole0, whole1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(whole0, sid)
+    for a, b in pairs:
+        tv.verify_attn_timed(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                             t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws,
+                             ws.numel(), a, b, stream=sid)
+    ev.record(whole1, sid)
+    torch.cuda.synchronize()
+    split_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    eager_ms = ev.elapsed_ms(whole0, whole1) / nrep
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    ev.destroy(whole0)
+    ev.destroy(whole1)
+    split_avg_ms = float(np.mean(split_ms))
+
+    kv_bytes, total_bytes, flops = algorithmic(w)
+    us_per_call = ms_per_step * 1e3
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    t_hbm = total_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma >= t_hbm:
+        achieved = flops / (split_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        achieved = total_bytes / (split_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["traffic"] = measured_traffic(args.config, splits)
+    roof["kernel"] = "tv_split_kernel"
+    roof["kernel_avg_us"] = split_avg_ms * 1e3
+    roof["algorithmic"] = {"bytes": total_bytes, "flops": flops,
+                           "floor_us": max(t_hbm, t_mfma) * 1e6}
+
+    res = {
+        "metric": "verify-attn µs/call + gathered-KV GB/s (% of MI355X HBM peak) at 32k prefix",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, bf16-rounded N(0,1))",
+        "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "eager_us_per_call": eager_ms * 1e3,
+        "floor_fraction": max(t_hbm, t_mfma) / (ms_per_step * 1e-3),
+        "config": {"workload": desc, "requests": w.batch, "n_draft": int(w.max_q_len),
+                   "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,
+                   "plan": plan, "out_dtype": "f32" if args.out_f32 else "bf16",
+                   "gathered_kv_bytes": kv_bytes, "visible_pairs_x_heads": w.visible_pairs() * H},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        o = out.float().cpu().numpy().astype(np.float64)
+        l = lse.cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline(w, o, l, kv_bytes, args.cpu_budget_s, args.out_f32)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

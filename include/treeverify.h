@@ -1,0 +1,167 @@
+/*
+ * treeverify.h -- tree-masked verify attention over a paged MLA latent KV pool,
+ * for AMD Instinct MI355X (gfx950).  C ABI of libtreeverify.so.
+ *
+ * The operation (sources: three pages about one verify-kernel bring-up):
+ *
+ *   Draft-tree query rows q[t, h, 0:576] (absorbed MLA: 512 latent + 64 RoPE
+ *   dims; page 3 "The Pivot to Live Cutover", section "Input Knowledge
+ *   Required") attend over keys gathered from a latent pool kv_buf[slot, 0:576]
+ *   with page size 1 (same section, and "The Technical Investigation", where the
+ *   MLA key buffer is [num_slots, 1, 576]).  The keys of request b are
+ *   kv_buf[kv_indices[kv_indptr[b] + j]], j = 0 .. L_b-1: the prefix slots
+ *   followed by the slots the draft tokens were written to (page 2 "Flipping
+ *   the Switch", section "The Long Road to Parity").  Draft row i of request b
+ *   may see key j iff mask[mask_indptr[b] + i*L_b + j] != 0; the mask block of a
+ *   request is n_b x L_b bytes with row stride L_b = prefix_len + n_draft (same
+ *   section: mask=(270,) = 9 x 30) and is located through mask_indptr (page 3,
+ *   section "The Technical Investigation").  All H heads of a draft share its
+ *   mask row.  With score s_j = sm_scale * <q[t,h,:], k_j[0:576]> over the
+ *   visible keys:
+ *
+ *       out[t,h,d] = sum_j softmax(s)_j * k_j[d],  d < 512   (V = first 512 dims)
+ *       lse[t,h]   = ln sum_j exp(s_j)
+ *
+ *   A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Method: KV-split flash decoding (page 2, section "The Broader Context": the
+ * KV length is cut into splits that run in parallel, each yielding a partial
+ * output and log-sum-exp) followed by an LSE merge.  The call is capture-safe
+ * (page 2, section "The Decision to Flip the Switch": no host syncs, copies or
+ * allocations): it only enqueues kernels on `stream`.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_QK_DIM 576 /* key / query dims: 512 latent + 64 RoPE */
+#define TV_V_DIM 512  /* value dims: the first 512 latent dims  */
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  TV_ERR_SHAPE = 2,       /* a size in tv_problem is out of range or inconsistent        */
+  TV_ERR_WORKSPACE = 3,   /* workspace is NULL or smaller than tv_workspace_bytes()      */
+  TV_ERR_UNSUPPORTED = 4, /* out_dtype unknown                                           */
+  TV_ERR_INPUT = 5,       /* tv_check_inputs found a device-side precondition violated   */
+  TV_ERR_LAUNCH = 6,      /* a kernel launch failed (e.g. the current device is not gfx950) */
+  TV_ERR_HIP = 7          /* a HIP runtime call inside tv_check_inputs failed            */
+} tv_status;
+
+typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
+
+/* Host-side description of one call.  Device-side lengths may vary between
+ * calls (or graph replays) as long as they stay within these bounds. */
+typedef struct tv_problem {
+  int32_t batch;      /* B >= 0 requests                                             */
+  int32_t num_heads;  /* H >= 1 query heads sharing one latent KV head               */
+  int64_t total_q;    /* rows of q / out / lse (draft tokens), >= qo_indptr[B]       */
+  int32_t max_q_len;  /* >= every n_b = qo_indptr[b+1] - qo_indptr[b]                */
+  int32_t max_kv_len; /* >= every L_b = kv_indptr[b+1] - kv_indptr[b], draft slots
+                         INCLUDED (L_b = prefix_len + n_draft)                        */
+  int64_t num_slots;  /* rows of kv_buf                                              */
+  int64_t total_kv;   /* entries of kv_indices, >= kv_indptr[B]; < 2^31              */
+  int64_t total_mask; /* bytes of mask, >= mask_indptr[B]; < 2^31                     */
+  int32_t num_splits; /* 0: chosen by the library.  k > 0: the longest request
+                         (max_kv_len keys) is cut into k splits of equal size,
+                         rounded up to the 32-key tile; shorter requests use as
+                         many splits of that size as they need                      */
+  int32_t out_dtype;  /* tv_out_dtype                                                */
+} tv_problem;
+
+/* Launch plan that tv_verify_attn uses for `p` (host arithmetic only). */
+typedef struct tv_plan {
+  int32_t split_keys;  /* keys per split (multiple of 32)                           */
+  int32_t max_splits;  /* splits of the longest request                             */
+  int32_t row_blocks;  /* 128-row blocks of the largest request (n_b * H rows)      */
+  int32_t merge;       /* 1 if the merge kernel runs (max_splits > 1)               */
+  int64_t workspace_bytes;
+} tv_plan;
+
+/* Fills *plan for `p`.  TV_ERR_NULL / TV_ERR_SHAPE on bad arguments. */
+tv_status tv_get_plan(const tv_problem* p, tv_plan* plan);
+
+/* Bytes of device workspace tv_verify_attn needs for `p` (0 if `p` is invalid
+ * or there is nothing to compute).  It holds one 32-bit visibility word per
+ * (draft token, 32-key tile) and, when more than one split is used, the
+ * per-split partial outputs (total_q * H * max_splits * (512 + 1) fp32). */
+size_t tv_workspace_bytes(const tv_problem* p);
+
+/*
+ * Tree-masked verify attention.  All pointers are device memory owned by the
+ * caller; the library keeps no state between calls and allocates nothing.
+ *
+ *   q           bf16 [total_q, H, 576], contiguous
+ *   kv_buf      bf16 [num_slots, 576], contiguous (1152-byte rows), 16-byte aligned
+ *   kv_indices  int32 [total_kv]: per request, prefix slots then draft slots
+ *   kv_indptr   int32 [B+1], non-decreasing
+ *   qo_indptr   int32 [B+1], non-decreasing; request b owns q rows
+ *               qo_indptr[b] .. qo_indptr[b+1]-1
+ *   mask        uint8 [total_mask], nonzero = visible
+ *   mask_indptr int32 [B+1]; mask_indptr[b+1] - mask_indptr[b] = n_b * L_b
+ *   sm_scale    score scale (e.g. 1/sqrt(192))
+ *   out         [total_q, H, 512] bf16 (round to nearest even) or fp32
+ *   lse         fp32 [total_q, H], natural log
+ *   workspace   >= tv_workspace_bytes(p) bytes, 256-byte aligned; contents on
+ *               entry are ignored.  May be NULL when that size is 0.
+ *   stream      hipStream_t (NULL = default stream)
+ *
+ * q rows outside every request are left untouched.
+ *
+ * Errors: host-detectable problems return TV_ERR_* before anything is enqueued
+ * (outputs untouched).  Device-content problems (decreasing indptrs, slots
+ * outside the pool, L_b < n_b, a mask block that is not n_b * L_b bytes,
+ * lengths above the tv_problem bounds) are undefined behaviour here; run
+ * tv_check_inputs to detect them.  Concurrent calls need distinct workspaces.
+ * Preconditions: the draft tokens' latent rows are already in kv_buf at their
+ * slots, every referenced row is finite, and out/lse alias no input.
+ */
+tv_status tv_verify_attn(const tv_problem* p, const void* q, const void* kv_buf,
+                         const int32_t* kv_indices, const int32_t* kv_indptr,
+                         const int32_t* qo_indptr, const uint8_t* mask,
+                         const int32_t* mask_indptr, float sm_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement variant of tv_verify_attn: the same arguments and the same
+ * kernels, plus two caller-created hipEvent_t handles recorded on `stream`
+ * immediately before and after the split-attention kernel (the dominant one),
+ * so a benchmark can time that kernel alone.  Either event may be NULL.
+ */
+tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* kv_buf,
+                               const int32_t* kv_indices, const int32_t* kv_indptr,
+                               const int32_t* qo_indptr, const uint8_t* mask,
+                               const int32_t* mask_indptr, float sm_scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* split_start_event, void* split_stop_event, void* stream);
+
+/*
+ * Debug validator for the device-side preconditions of tv_verify_attn.  Copies
+ * the three indptr arrays and kv_indices to the host and synchronises `stream`:
+ * NOT capture-safe.  Returns TV_OK, TV_ERR_INPUT (a precondition is violated;
+ * *bad_request, if not NULL, receives the first offending request, else -1),
+ * TV_ERR_HIP if a copy fails, or the host-side errors of tv_verify_attn.  Checks:
+ * indptrs non-decreasing and within total_q / total_kv / total_mask; every
+ * n_b <= max_q_len and L_b <= max_kv_len; L_b >= n_b; the mask block of
+ * request b is exactly n_b * L_b bytes; every slot in [0, num_slots).  The last
+ * two catch both halves of the marshaling mistake the pages describe (page 2,
+ * section "The Long Road to Parity"): draft slots missing from kv_indices, and
+ * a mask laid out with the prefix-only row stride.  Mask contents are not read.
+ */
+tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
+                          const int32_t* kv_indptr, const int32_t* qo_indptr,
+                          const int32_t* mask_indptr, void* stream, int32_t* bad_request);
+
+/* Static description of a status code. */
+const char* tv_status_str(tv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREEVERIFY_H */

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI: no GPU needed, no kernel is launched.
+
+Every call here fails argument validation before the library touches the HIP
+runtime, or is pure host arithmetic (plan, workspace size, status strings).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_verify_mla_paged_amd as tv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "treeverify.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert set(declared) == set(tv.EXPORTS)
+    for name in declared:
+        assert hasattr(tv.lib(), name), name
+
+
+def test_status_strings():
+    for code in range(8):
+        assert tv.status_str(code) and tv.status_str(code) != "unknown status"
+    assert tv.status_str(99) == "unknown status"
+
+
+def prob(**kw):
+    base = dict(batch=1, num_heads=8, total_q=9, max_q_len=9, max_kv_len=30, num_slots=4096,
+                total_kv=30, total_mask=270, num_splits=0, out_dtype=tv.OUT_BF16)
+    base.update(kw)
+    return tv.make_problem(**base)
+
+
+def test_plan_live_shape_is_one_split():
+    pl = tv.plan(prob())
+    assert pl["max_splits"] == 1 and pl["merge"] == 0 and pl["row_blocks"] == 1
+    assert pl["split_keys"] % 32 == 0 and pl["split_keys"] >= 30
+    # visibility words only: 9 drafts x 1 tile x 4 bytes, 256-byte aligned
+    assert pl["workspace_bytes"] == 256 == tv.workspace_bytes(prob())
+
+
+def test_plan_explicit_splits_cover_the_longest_request():
+    p = prob(batch=1, num_heads=16, total_q=32, max_q_len=32, max_kv_len=32800, num_slots=200000,
+             total_kv=32800, total_mask=32 * 32800, num_splits=32)
+    pl = tv.plan(p)
+    assert pl["split_keys"] % 32 == 0
+    assert pl["max_splits"] * pl["split_keys"] >= 32800
+    assert (pl["max_splits"] - 1) * pl["split_keys"] < 32800
+    assert pl["max_splits"] <= 32 and pl["merge"] == 1 and pl["row_blocks"] == 4
+    rows = 32 * 16
+    words = -(-(32 * 1025 * 4) // 256) * 256
+    parts = -(-(rows * pl["max_splits"] * 512 * 4) // 256) * 256 + \
+        -(-(rows * pl["max_splits"] * 4) // 256) * 256
+    assert pl["workspace_bytes"] == words + parts
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 7, 16, 64, 128, 1000, 5000])
+def test_plan_split_count_bounds(k):
+    p = prob(max_kv_len=32777, total_kv=32777, total_mask=9 * 32777, num_splits=k)
+    pl = tv.plan(p)
+    assert pl["max_splits"] <= k
+    assert pl["max_splits"] * pl["split_keys"] >= 32777
+
+
+def test_plan_heuristic_fills_the_chip():
+    # 1 request, 512 rows (4 row blocks), 32800 keys: about one workgroup per CU
+    p = prob(num_heads=16, total_q=32, max_q_len=32, max_kv_len=32800, total_kv=32800,
+             total_mask=32 * 32800, num_slots=200000)
+    pl = tv.plan(p)
+    assert 200 <= pl["max_splits"] * pl["row_blocks"] <= 256
+
+
+def test_bad_shapes_are_rejected():
+    for kw in [dict(num_heads=0), dict(batch=-1), dict(max_kv_len=-1), dict(num_splits=-2),
+               dict(total_kv=2 ** 31), dict(max_q_len=10, total_q=9)]:
+        assert tv.workspace_bytes(prob(**kw)) == 0
+        with pytest.raises(tv.TreeVerifyError) as e:
+            tv.plan(prob(**kw))
+        assert e.value.code == 2
+    with pytest.raises(tv.TreeVerifyError) as e:
+        tv.plan(prob(out_dtype=7))
+    assert e.value.code == 4
+
+
+def test_null_pointers_and_short_workspace_fail_before_any_launch():
+    p = prob()
+    fake = 1 << 20  # aligned non-null stand-in; never dereferenced on these paths
+    args = [fake] * 7
+    # q missing
+    assert tv.verify_attn_status(p, 0, *args[1:7], 0.07, fake, fake, fake, 1 << 20) == 1
+    # out missing
+    assert tv.verify_attn_status(p, *args, 0.07, 0, fake, fake, 1 << 20) == 1
+    # workspace missing / too small / misaligned
+    assert tv.verify_attn_status(p, *args, 0.07, fake, fake, 0, 0) == 3
+    assert tv.verify_attn_status(p, *args, 0.07, fake, fake, fake, 255) == 3
+    assert tv.verify_attn_status(p, *args, 0.07, fake, fake, fake + 16, 1 << 20) == 3
+    # misaligned kv_buf
+    assert tv.verify_attn_status(p, fake, fake + 2, *args[2:7], 0.07, fake, fake, fake,
+                                 1 << 20) == 2
+    # bad problem
+    assert tv.verify_attn_status(prob(num_heads=0), *args, 0.07, fake, fake, fake, 1 << 20) == 2
+
+
+def test_empty_problem_is_a_no_op():
+    p = prob(batch=0, total_q=0, max_q_len=0)
+    assert tv.workspace_bytes(p) == 0
+    assert tv.verify_attn_status(p, 0, 0, 0, 0, 0, 0, 0, 0.07, 0, 0, 0, 0) == 0
+    assert tv.check_inputs(p, 0, 0, 0, 0, stream=0) == (0, -1)
+
+
+def test_check_inputs_validates_host_arguments_first():
+    assert tv.check_inputs(prob(), 0, 0, 0, 0, stream=0)[0] == 1
+    assert tv.check_inputs(prob(num_heads=0), 0, 0, 0, 0, stream=0)[0] == 2
+
+
+def test_problem_struct_layout_matches_header():
+    # int32, int32, int64, int32, int32, int64, int64, int64, int32, int32
+    assert ctypes.sizeof(tv.Problem) == 56
+    assert tv.Problem.num_splits.offset == 48 and tv.Problem.out_dtype.offset == 52
+    assert ctypes.sizeof(tv.Plan) == 24

@@ -1,0 +1,292 @@
+"""Parity of the HIP path (called through the C ABI) against the fp64 oracle.
+
+Bar (floating point): max |out - oracle| <= 8e-3 and sum|diff| / sum|oracle| <=
+2e-3 on bf16-rounded inputs; a bf16 output may additionally differ by half a
+bf16 ulp of the reference where |o| >= 2 (its own rounding).  lse: derived from
+fp32 accumulation of 576-term scores, |diff| <= 2e-4 * max(1, |lse|).
+Visibility handling is checked exactly (same visible-key set per row) and
+results are checked to be independent of the split count (lse within 1e-5).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tv_workload as W
+from gpu_util import GpuCall, compare, run, sample_rows, upload
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU present", allow_module_level=True)
+
+import tree_verify_mla_paged_amd as tv  # noqa: E402  (fails loudly if the library is missing)
+
+
+def full_check(w, num_splits=0, out_f32=False, label=""):
+    ro, rl = oracle.run(w)
+    o, l = run(w, num_splits=num_splits, out_f32=out_f32)
+    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label)
+
+
+def sampled_check(w, nrows, num_splits=0, out_f32=False, label="", seed=0):
+    rows = sample_rows(w, nrows, seed)
+    ro, rl = oracle.run(w, rows=rows)
+    o, l = run(w, num_splits=num_splits, out_f32=out_f32)
+    H = w.num_heads
+    o = o.reshape(-1, 512)[rows]
+    l = l.reshape(-1)[rows]
+    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label)
+
+
+# ------------------------------------------------------------- the configs
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_c1_live_shape(out_f32):
+    print("C1 out_f32=%s" % out_f32, flush=True)
+    full_check(W.config(1), out_f32=out_f32, label="C1")
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_c2_segmented_batch(out_f32):
+    print("C2 out_f32=%s" % out_f32, flush=True)
+    full_check(W.config(2), out_f32=out_f32, label="C2")
+
+
+@pytest.mark.parametrize("num_splits", [0, 32])
+def test_c3_32k_prefix(num_splits):
+    print("C3 num_splits=%d" % num_splits, flush=True)
+    sampled_check(W.config(3), 96, num_splits=num_splits, label="C3")
+
+
+def test_c4_200k_prefix():
+    print("C4", flush=True)
+    sampled_check(W.config(4), 48, label="C4")
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_c5_large_batch_with_outliers(out_f32):
+    print("C5 out_f32=%s" % out_f32, flush=True)
+    sampled_check(W.config(5), 96, out_f32=out_f32, label="C5")
+
+
+def test_long_prefix_live_shape():
+    print("S1 (32k prefix, n=9, H=8)", flush=True)
+    sampled_check(W.sweep(1), 72, label="S1")
+
+
+# ------------------------------------------------ small shapes, every path
+
+SMALL = [
+    # seed, prefix lengths, draft counts, heads, num_splits
+    (201, [100], [5], 8, 0),          # 4 tiles, ragged tail
+    (202, [100], [5], 8, 3),          # 3 splits, ragged last split
+    (203, [0], [1], 1, 0),            # one key
+    (204, [31], [2], 1, 0),           # 33 keys: tile + 1
+    (205, [64], [1], 3, 5),           # H not dividing 128
+    (206, [300, 7, 0, 95], [3, 2, 0, 6], 5, 4),  # batch with an empty request
+    (207, [250], [20], 16, 2),        # 320 rows: 3 row blocks, last partial
+    (208, [40], [2], 64, 0),          # all heads of a model
+    (209, [129], [4], 128, 3),        # 512 rows at H=128
+    (210, [1000], [9], 8, 7),         # many splits, several tiles each
+    (211, [5, 600, 33], [1, 24, 3], 64, 0),
+]
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H,ns", SMALL)
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_small_shapes(seed, prefix, ndraft, H, ns, out_f32):
+    print("small seed=%d H=%d ns=%d f32=%s" % (seed, H, ns, out_f32), flush=True)
+    w = W.small(seed, prefix, ndraft, num_heads=H)
+    full_check(w, num_splits=ns, out_f32=out_f32, label="small%d" % seed)
+
+
+def test_random_masks_many_splits():
+    """Masks that are not trees (arbitrary visibility, rows with no visible key)."""
+    w = W.small(220, [90, 13], [7, 4], num_heads=4)
+    rng = np.random.default_rng(220)
+    w.mask[:] = (rng.random(w.mask.size) < 0.3).astype(np.uint8)
+    L0 = int(w.kv_lens[0])
+    w.mask[2 * L0:3 * L0] = 0  # draft 2 of request 0 sees nothing
+    for ns in (1, 2, 4):
+        print("random masks ns=%d" % ns, flush=True)
+        full_check(w, num_splits=ns, out_f32=True, label="randmask ns=%d" % ns)
+
+
+# ------------------------------------------------- split-count invariance
+
+def test_split_count_invariance():
+    w = W.config(3)
+    rows = sample_rows(w, 64, seed=3)
+    ref_o = ref_l = None
+    for ns in (1, 2, 3, 7, 16, 32, 64, 128):
+        print("C3 split invariance ns=%d" % ns, flush=True)
+        g = GpuCall(w, num_splits=ns, out_f32=True)
+        g.call()
+        o, l = g.result()
+        o = o.reshape(-1, 512)
+        l = l.reshape(-1)
+        if ref_o is None:
+            ref_o, ref_l = o, l
+            ro, rl = oracle.run(w, rows=rows)
+            compare(o[rows], l[rows], ro, rl, bf16_out=False, label="C3 ns=1")
+            continue
+        assert np.abs(l - ref_l).max() <= 1e-5, ns
+        assert np.abs(o - ref_o).max() <= 1e-4, ns
+
+
+# ------------------------------------------------------ exact visibility
+
+def test_visible_key_set_is_exact():
+    """q = 0 makes every visible score 0, so each visible key gets weight exactly
+    1/n_vis.  With V[j] = e_(j mod 512), n_vis * out recovers the visible set."""
+    for seed, L_pref, n in ((230, 300, 6), (231, 20, 12)):
+        w = W.small(seed, [L_pref], [n], num_heads=3)
+        rng = np.random.default_rng(seed)
+        w.mask[:] = (rng.random(w.mask.size) < 0.5).astype(np.uint8)
+        L = int(w.kv_lens[0])
+        assert L <= 512
+        w.q[:] = 0
+        vals = np.zeros((L, 576), np.float32)
+        vals[np.arange(L), np.arange(L) % 512] = 1.0
+        w.kv[w.kv_indices] = W.bf16_round(vals)
+        o, l = run(w, out_f32=True)
+        m = w.mask.reshape(n, L)
+        for i in range(n):
+            nv = int(m[i].sum())
+            for h in range(3):
+                if nv == 0:
+                    assert l[i, h] == -np.inf and np.all(o[i, h] == 0)
+                    continue
+                got = np.rint(o[i, h, :L] * nv).astype(int)
+                assert np.array_equal(got, m[i].astype(int)), (seed, i, h)
+                assert abs(l[i, h] - np.log(nv)) < 1e-6
+
+
+def test_invisible_sentinel_key_never_leaks():
+    """One invisible key per row would dominate the softmax by e^30 if it leaked."""
+    w = W.small(232, [77], [5], num_heads=2)
+    L = int(w.kv_lens[0])
+    qf = W.bf16_to_f32(w.q).astype(np.float64)
+    for i in range(5):
+        j = (13 * i + 7) % L
+        w.mask[i * L + j] = 0
+        # make key j score about +30 above the others for both heads of draft i
+        k = qf[i].sum(axis=0)
+        k = k / np.linalg.norm(k) * (30.0 / float(w.sm_scale)) / np.linalg.norm(qf[i], axis=1).mean()
+        w.kv[w.kv_indices[j]] = W.bf16_round(k.astype(np.float32))
+    full_check(w, out_f32=True, label="sentinel")
+
+
+def test_single_visible_key_returns_its_value_bits():
+    w = W.small(233, [70], [6], num_heads=4)
+    L = int(w.kv_lens[0])
+    w.mask[:] = 0
+    picks = [0, 31, 32, 50, L - 1, 64]
+    for i, j in enumerate(picks):
+        w.mask[i * L + j] = 1
+    g = GpuCall(w, num_splits=2)
+    g.call()
+    bits = g.out_bits().view(np.uint16)
+    for i, j in enumerate(picks):
+        v = w.kv[w.kv_indices[j], :512]
+        for h in range(4):
+            assert np.array_equal(bits[i, h], v), (i, j, h)
+
+
+# --------------------------------------------------------- invariances
+
+def test_slot_permutation_is_bit_identical():
+    w = W.config(2)
+    a = GpuCall(w, out_f32=True)
+    a.call()
+    rng = np.random.default_rng(5)
+    pi = rng.permutation(w.num_slots)
+    kv2 = np.empty_like(w.kv)
+    kv2[pi] = w.kv
+    w2 = W.Workload(**{**w.__dict__, "kv": kv2, "kv_indices": pi[w.kv_indices].astype(np.int32)})
+    b = GpuCall(w2, out_f32=True)
+    b.call()
+    assert np.array_equal(a.out_bits(), b.out_bits())
+    assert np.array_equal(a.lse.cpu().numpy(), b.lse.cpu().numpy())
+
+
+def test_repeat_calls_are_deterministic():
+    w = W.config(3)
+    g = GpuCall(w)
+    g.call()
+    first = g.out_bits().copy()
+    l1 = g.lse.cpu().numpy().copy()
+    for _ in range(2):
+        g.call()
+        assert np.array_equal(g.out_bits(), first)
+        assert np.array_equal(g.lse.cpu().numpy(), l1)
+
+
+def test_score_jump_beyond_headroom_restarts_the_split():
+    """A row whose maximum jumps by far more than 2^64 after its first tile."""
+    w = W.small(240, [400], [4], num_heads=2)
+    L = int(w.kv_lens[0])
+    qv = W.bf16_to_f32(w.q).copy()
+    qv[1, 0, :] = 0
+    qv[1, 0, 7] = 40.0
+    w.q[:] = W.bf16_round(qv)
+    k = W.bf16_to_f32(w.kv[w.kv_indices[300]]).copy()
+    k[7] = 40.0  # score 0.072 * 1600 = 115 natural units above the rest
+    w.kv[w.kv_indices[300]] = W.bf16_round(k)
+    for ns in (1, 3):
+        full_check(w, num_splits=ns, out_f32=True, label="jump ns=%d" % ns)
+
+
+# ------------------------------------------------------------ capture
+
+def test_hip_graph_capture_and_replay():
+    w1 = W.config(2)
+    w2 = W.config(2)
+    # same shapes and bounds, different content: seed a second copy of the inputs
+    rng = np.random.default_rng(77)
+    w2 = W.Workload(**{**w1.__dict__, "q": W.bf16_round(rng.standard_normal(w1.q.shape,
+                                                                             dtype=np.float32))})
+    g = GpuCall(w1)
+    g.call()
+    eager = g.out_bits().copy()
+    eager_l = g.lse.cpu().numpy().copy()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        g.call(stream=stream)
+    for rep in range(3):
+        g.out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g.out_bits(), eager), rep
+        assert np.array_equal(g.lse.cpu().numpy(), eager_l), rep
+    # new device-side content, same bounds: the replay follows it
+    g.t["q"].copy_(torch.from_numpy(w2.q.view(np.int16)).cuda())
+    graph.replay()
+    torch.cuda.synchronize()
+    o, l = g.result()
+    ro, rl = oracle.run(w2)
+    compare(o, l, ro, rl, bf16_out=True, label="replay")
+
+
+# ------------------------------------------------------- input checking
+
+def test_check_inputs_catches_the_marshaling_bug():
+    w = W.config(1)
+    t = upload(w)
+    p = tv.make_problem(1, 8, 9, 9, 30, w.num_slots, 30, 270)
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                           t["mask_indptr"]) == (0, -1)
+    # draft slots missing from kv_indices (L = 21) with the mask at stride 30
+    kvp = torch.tensor([0, 21], dtype=torch.int32, device="cuda")
+    assert tv.check_inputs(p, t["kv_indices"], kvp, t["qo_indptr"], t["mask_indptr"]) == (5, 0)
+    # drafts present, mask laid out with the prefix-only stride (9 x 21 bytes)
+    mp = torch.tensor([0, 189], dtype=torch.int32, device="cuda")
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"], mp) == (5, 0)
+    # a slot outside the pool
+    bad = t["kv_indices"].clone()
+    bad[3] = w.num_slots
+    assert tv.check_inputs(p, bad, t["kv_indptr"], t["qo_indptr"], t["mask_indptr"]) == (5, 0)

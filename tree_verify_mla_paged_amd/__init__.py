@@ -1,0 +1,166 @@
+"""Python binding of libtreeverify (tree-masked verify attention, MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libtreeverify.so, called through its C ABI (include/treeverify.h).
+torch is used for device memory and streams; tensors are passed by pointer.
+There is no fallback: if the library is missing this module fails to import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libtreeverify.so")
+
+QK_DIM = 576
+V_DIM = 512
+OUT_BF16 = 0
+OUT_F32 = 1
+
+STATUS = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_WORKSPACE",
+          4: "TV_ERR_UNSUPPORTED", 5: "TV_ERR_INPUT", 6: "TV_ERR_LAUNCH", 7: "TV_ERR_HIP"}
+
+EXPORTS = ("tv_get_plan", "tv_workspace_bytes", "tv_verify_attn", "tv_verify_attn_timed",
+           "tv_check_inputs",
+           "tv_status_str")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("max_q_len", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("num_slots", ctypes.c_int64),
+                ("total_kv", ctypes.c_int64), ("total_mask", ctypes.c_int64),
+                ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("split_keys", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("row_blocks", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s: %s (%s)" % (where, status_str(code), STATUS.get(code, code)))
+        self.code = code
+
+
+# The library and torch must share one HIP runtime.  torch ships its own
+# libamdhip64; loading it first makes libtreeverify's libamdhip64 dependency
+# resolve to that copy instead of a second runtime whose device pointers and
+# streams would not be torch's.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIBRARY_PATH):
+    raise ImportError("libtreeverify.so is not built: run `python -m tree_verify_mla_paged_amd.build` "
+                      "(hipcc, gfx950) before using the GPU path")
+
+_lib = ctypes.CDLL(LIBRARY_PATH)
+_P = ctypes.POINTER(Problem)
+_vp = ctypes.c_void_p
+_lib.tv_get_plan.argtypes = [_P, ctypes.POINTER(Plan)]
+_lib.tv_get_plan.restype = ctypes.c_int
+_lib.tv_workspace_bytes.argtypes = [_P]
+_lib.tv_workspace_bytes.restype = ctypes.c_size_t
+_lib.tv_verify_attn.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                _vp, ctypes.c_size_t, _vp]
+_lib.tv_verify_attn.restype = ctypes.c_int
+_lib.tv_verify_attn_timed.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                      _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
+_lib.tv_verify_attn_timed.restype = ctypes.c_int
+_lib.tv_check_inputs.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_int32)]
+_lib.tv_check_inputs.restype = ctypes.c_int
+_lib.tv_status_str.argtypes = [ctypes.c_int]
+_lib.tv_status_str.restype = ctypes.c_char_p
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return _lib.tv_status_str(int(code)).decode()
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def make_problem(batch: int, num_heads: int, total_q: int, max_q_len: int, max_kv_len: int,
+                 num_slots: int, total_kv: int, total_mask: int, num_splits: int = 0,
+                 out_dtype: int = OUT_BF16) -> Problem:
+    return Problem(batch, num_heads, total_q, max_q_len, max_kv_len, num_slots, total_kv,
+                   total_mask, num_splits, out_dtype)
+
+
+def plan(problem: Problem) -> dict:
+    pl = Plan()
+    rc = _lib.tv_get_plan(ctypes.byref(problem), ctypes.byref(pl))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tv_get_plan")
+    return {f: getattr(pl, f) for f, _ in Plan._fields_}
+
+
+def workspace_bytes(problem: Problem) -> int:
+    return int(_lib.tv_workspace_bytes(ctypes.byref(problem)))
+
+
+def verify_attn(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr,
+                sm_scale: float, out, lse, workspace, workspace_nbytes: int = None, stream=None):
+    """Enqueue tv_verify_attn on `stream` (default: torch's current stream).
+    Tensors are device tensors (or raw device pointers as ints)."""
+    if workspace_nbytes is None:
+        workspace_nbytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
+    rc = _lib.tv_verify_attn(ctypes.byref(problem), _ptr(q), _ptr(kv_buf), _ptr(kv_indices),
+                             _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
+                             float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                             int(workspace_nbytes), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tv_verify_attn")
+
+
+def verify_attn_timed(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask,
+                      mask_indptr, sm_scale: float, out, lse, workspace, workspace_nbytes: int,
+                      split_start_event: int, split_stop_event: int, stream=None):
+    """tv_verify_attn_timed: events (raw hipEvent_t handles) bracket the split kernel."""
+    rc = _lib.tv_verify_attn_timed(ctypes.byref(problem), _ptr(q), _ptr(kv_buf), _ptr(kv_indices),
+                                   _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
+                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                   int(workspace_nbytes), int(split_start_event),
+                                   int(split_stop_event), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tv_verify_attn_timed")
+
+
+def verify_attn_status(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask,
+                       mask_indptr, sm_scale: float, out, lse, workspace, workspace_nbytes: int,
+                       stream: int = 0) -> int:
+    """Same call, returning the raw status code (for argument-checking tests)."""
+    return int(_lib.tv_verify_attn(ctypes.byref(problem), _ptr(q), _ptr(kv_buf), _ptr(kv_indices),
+                                   _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
+                                   float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                   int(workspace_nbytes), int(stream)))
+
+
+def check_inputs(problem: Problem, kv_indices, kv_indptr, qo_indptr, mask_indptr, stream=None):
+    """Run tv_check_inputs; returns (status, first bad request or -1)."""
+    bad = ctypes.c_int32(-1)
+    rc = _lib.tv_check_inputs(ctypes.byref(problem), _ptr(kv_indices), _ptr(kv_indptr),
+                              _ptr(qo_indptr), _ptr(mask_indptr), _stream(stream),
+                              ctypes.byref(bad))
+    return int(rc), int(bad.value)

@@ -1,0 +1,281 @@
+// C-ABI host layer of libtreeverify: argument checks, launch plan, launches.
+//
+// tv_verify_attn enqueues up to three kernels on the caller's stream (mask
+// packing, split attention, LSE merge) and nothing else: no allocation, copy,
+// memset or synchronisation, so the call can be captured into a HIP graph
+// (page 2 "Flipping the Switch", section "The Decision to Flip the Switch":
+// the verify kernel consumes the serving stack's static buffers with no host
+// syncs, copies or allocations).  The KV split count follows the pages'
+// occupancy argument (page 2, section "The Broader Context": more KV splits to
+// fill the machine) re-derived for 256 compute units and one 128-row
+// workgroup per unit.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "tv_kernels.h"
+#include "treeverify.h"
+
+static_assert(sizeof(tv_problem) == 56 && offsetof(tv_problem, total_q) == 8 &&
+                  offsetof(tv_problem, num_slots) == 24 && offsetof(tv_problem, out_dtype) == 52,
+              "tv_problem layout is part of the ABI");
+static_assert(sizeof(tv_plan) == 24 && offsetof(tv_plan, workspace_bytes) == 16,
+              "tv_plan layout is part of the ABI");
+
+namespace {
+
+constexpr int64_t kMaxInt32 = 2147483647;
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kMinSplitTiles = 8;  // keys per split >= 256 unless the caller asks otherwise
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct Layout {
+  tv_plan plan;
+  int32_t max_tiles;     // 32-key tiles of the longest request
+  int64_t words_off, words_bytes;
+  int64_t wso_off, wso_bytes;
+  int64_t wsl_off, wsl_bytes;
+  bool active;           // anything to compute
+};
+
+tv_status make_layout(const tv_problem* p, Layout* lay) {
+  if (!p || !lay) return TV_ERR_NULL;
+  std::memset(lay, 0, sizeof *lay);
+  if (p->batch < 0 || p->num_heads < 1 || p->total_q < 0 || p->max_q_len < 0 ||
+      p->max_kv_len < 0 || p->num_slots < 0 || p->total_kv < 0 || p->total_mask < 0 ||
+      p->num_splits < 0)
+    return TV_ERR_SHAPE;
+  if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL)
+    return TV_ERR_SHAPE;
+  if (p->out_dtype != TV_OUT_BF16 && p->out_dtype != TV_OUT_F32) return TV_ERR_UNSUPPORTED;
+  if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
+  if ((int64_t)p->max_q_len * p->num_heads > kMaxInt32 ||
+      p->total_q * (int64_t)p->num_heads > kMaxInt32)
+    return TV_ERR_SHAPE;
+  lay->active = p->batch > 0 && p->total_q > 0 && p->max_q_len > 0;
+  if (!lay->active) return TV_OK;
+
+  const int64_t L = p->max_kv_len;
+  const int64_t rows_max = (int64_t)p->max_q_len * p->num_heads;
+  const int64_t row_blocks = ceil_div(rows_max, tv::ROWS_PER_WG);
+  int64_t split_keys;
+  if (L == 0) {
+    split_keys = tv::TILE_KEYS;
+  } else if (p->num_splits > 0) {
+    split_keys = ceil_div(ceil_div(L, p->num_splits), tv::TILE_KEYS) * tv::TILE_KEYS;
+  } else {
+    // one workgroup per compute unit over the whole batch, splits of >= 8 tiles
+    const int64_t kv_tiles = ceil_div(std::max<int64_t>(p->total_kv, L), tv::TILE_KEYS);
+    const int64_t per_wg = std::max<int64_t>(kMinSplitTiles, ceil_div(row_blocks * kv_tiles, kCUs));
+    split_keys = std::min<int64_t>(per_wg, ceil_div(L, tv::TILE_KEYS)) * tv::TILE_KEYS;
+  }
+  const int64_t max_splits = std::max<int64_t>(1, ceil_div(L, split_keys));
+  const int64_t total_work = (int64_t)p->batch * max_splits * row_blocks;
+  if (total_work > kMaxInt32 - 8) return TV_ERR_SHAPE;
+
+  lay->max_tiles = (int32_t)std::max<int64_t>(1, ceil_div(L, tv::TILE_KEYS));
+  lay->words_off = 0;
+  lay->words_bytes = align256(p->total_q * lay->max_tiles * 4);
+  int64_t off = lay->words_bytes;
+  if (max_splits > 1) {
+    const int64_t prow = p->total_q * p->num_heads * max_splits;
+    lay->wso_off = off;
+    lay->wso_bytes = align256(prow * TV_V_DIM * 4);
+    off += lay->wso_bytes;
+    lay->wsl_off = off;
+    lay->wsl_bytes = align256(prow * 4);
+    off += lay->wsl_bytes;
+  }
+  lay->plan.split_keys = (int32_t)split_keys;
+  lay->plan.max_splits = (int32_t)max_splits;
+  lay->plan.row_blocks = (int32_t)row_blocks;
+  lay->plan.merge = max_splits > 1;
+  lay->plan.workspace_bytes = off;
+  return TV_OK;
+}
+
+}  // namespace
+
+namespace {
+
+tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
+                 const int32_t* kv_indices, const int32_t* kv_indptr, const int32_t* qo_indptr,
+                 const uint8_t* mask, const int32_t* mask_indptr, float sm_scale, void* out,
+                 float* lse, void* workspace, size_t workspace_bytes, hipEvent_t ev0,
+                 hipEvent_t ev1, void* stream) {
+  Layout lay;
+  tv_status st = make_layout(p, &lay);
+  if (st != TV_OK) return st;
+  if (!lay.active) return TV_OK;
+  if (!q || !kv_buf || !kv_indptr || !qo_indptr || !mask_indptr || !out || !lse)
+    return TV_ERR_NULL;
+  if (p->max_kv_len > 0 && (!kv_indices || !mask)) return TV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(kv_buf) & 15) || (reinterpret_cast<uintptr_t>(q) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return TV_ERR_SHAPE;
+  if (lay.plan.workspace_bytes > 0) {
+    if (!workspace || workspace_bytes < (size_t)lay.plan.workspace_bytes) return TV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_WORKSPACE;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* words = reinterpret_cast<uint32_t*>(ws + lay.words_off);
+
+  if (p->max_kv_len > 0) {
+    tv::PackParams pp;
+    pp.mask = mask;
+    pp.mask_indptr = mask_indptr;
+    pp.kv_indptr = kv_indptr;
+    pp.qo_indptr = qo_indptr;
+    pp.words = words;
+    pp.max_tiles = lay.max_tiles;
+    const int64_t gx = ceil_div((int64_t)p->max_q_len * lay.max_tiles, 8);
+    if (gx > kMaxInt32) return TV_ERR_SHAPE;
+    if (tv::launch_pack(pp, (int)gx, p->batch, s) != hipSuccess) return TV_ERR_LAUNCH;
+  }
+
+  tv::SplitParams sp;
+  sp.q = static_cast<const uint16_t*>(q);
+  sp.kv = static_cast<const uint16_t*>(kv_buf);
+  sp.kv_indices = kv_indices;
+  sp.kv_indptr = kv_indptr;
+  sp.qo_indptr = qo_indptr;
+  sp.mask_words = words;
+  sp.out = out;
+  sp.lse = lse;
+  sp.ws_o = lay.plan.merge ? reinterpret_cast<float*>(ws + lay.wso_off) : nullptr;
+  sp.ws_lse = lay.plan.merge ? reinterpret_cast<float*>(ws + lay.wsl_off) : nullptr;
+  sp.s.scale_log2 = (float)((double)sm_scale * 1.4426950408889634074);
+  sp.s.num_heads = p->num_heads;
+  sp.s.split_keys = lay.plan.split_keys;
+  sp.s.max_splits = lay.plan.max_splits;
+  sp.s.row_blocks = lay.plan.row_blocks;
+  sp.s.total_work = (int32_t)((int64_t)p->batch * lay.plan.max_splits * lay.plan.row_blocks);
+  sp.s.max_tiles = lay.max_tiles;
+  sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
+  const int grid = (int)ceil_div(sp.s.total_work, 8) * 8;
+  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return TV_ERR_LAUNCH;
+  if (tv::launch_split(sp, grid, p->out_dtype, s) != hipSuccess) return TV_ERR_LAUNCH;
+  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return TV_ERR_LAUNCH;
+
+  if (lay.plan.merge) {
+    tv::MergeParams mp;
+    mp.kv_indptr = kv_indptr;
+    mp.qo_indptr = qo_indptr;
+    mp.ws_o = sp.ws_o;
+    mp.ws_lse = sp.ws_lse;
+    mp.out = out;
+    mp.lse = lse;
+    mp.num_heads = p->num_heads;
+    mp.split_keys = lay.plan.split_keys;
+    mp.max_splits = lay.plan.max_splits;
+    const int64_t gx = ceil_div((int64_t)p->max_q_len * p->num_heads, 2);
+    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, s) != hipSuccess)
+      return TV_ERR_LAUNCH;
+  }
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tv_status tv_get_plan(const tv_problem* p, tv_plan* plan) {
+  if (!p || !plan) return TV_ERR_NULL;
+  Layout lay;
+  const tv_status st = make_layout(p, &lay);
+  if (st != TV_OK) return st;
+  *plan = lay.plan;
+  return TV_OK;
+}
+
+size_t tv_workspace_bytes(const tv_problem* p) {
+  Layout lay;
+  if (make_layout(p, &lay) != TV_OK) return 0;
+  return (size_t)lay.plan.workspace_bytes;
+}
+
+tv_status tv_verify_attn(const tv_problem* p, const void* q, const void* kv_buf,
+                         const int32_t* kv_indices, const int32_t* kv_indptr,
+                         const int32_t* qo_indptr, const uint8_t* mask,
+                         const int32_t* mask_indptr, float sm_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return verify(p, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, out,
+                lse, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* kv_buf,
+                               const int32_t* kv_indices, const int32_t* kv_indptr,
+                               const int32_t* qo_indptr, const uint8_t* mask,
+                               const int32_t* mask_indptr, float sm_scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* split_start_event, void* split_stop_event, void* stream) {
+  return verify(p, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, out,
+                lse, workspace, workspace_bytes, static_cast<hipEvent_t>(split_start_event),
+                static_cast<hipEvent_t>(split_stop_event), stream);
+}
+
+tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
+                          const int32_t* kv_indptr, const int32_t* qo_indptr,
+                          const int32_t* mask_indptr, void* stream, int32_t* bad_request) {
+  if (bad_request) *bad_request = -1;
+  Layout lay;
+  tv_status st = make_layout(p, &lay);
+  if (st != TV_OK) return st;
+  if (p->batch == 0) return TV_OK;
+  if (!kv_indptr || !qo_indptr || !mask_indptr) return TV_ERR_NULL;
+  if (p->total_kv > 0 && !kv_indices) return TV_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t nb = (size_t)p->batch + 1;
+  std::vector<int32_t> kvp(nb), qop(nb), mp(nb), idx((size_t)p->total_kv);
+  if (hipMemcpyAsync(kvp.data(), kv_indptr, nb * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(qop.data(), qo_indptr, nb * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(mp.data(), mask_indptr, nb * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return TV_ERR_HIP;
+  if (p->total_kv > 0 && hipMemcpyAsync(idx.data(), kv_indices, idx.size() * 4,
+                                        hipMemcpyDeviceToHost, s) != hipSuccess)
+    return TV_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return TV_ERR_HIP;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    const int64_t q0 = qop[b], q1 = qop[b + 1], k0 = kvp[b], k1 = kvp[b + 1];
+    const int64_t m0 = mp[b], m1 = mp[b + 1];
+    const bool bad = q0 < 0 || k0 < 0 || m0 < 0 || q1 < q0 || k1 < k0 || m1 < m0 ||
+                     q1 > p->total_q || k1 > p->total_kv || m1 > p->total_mask ||
+                     q1 - q0 > p->max_q_len || k1 - k0 > p->max_kv_len ||
+                     k1 - k0 < q1 - q0 ||               // draft slots missing from kv_indices
+                     m1 - m0 != (q1 - q0) * (k1 - k0);  // mask stride is not L_b
+    if (bad) {
+      if (bad_request) *bad_request = b;
+      return TV_ERR_INPUT;
+    }
+    for (int64_t j = k0; j < k1; ++j) {
+      if (idx[j] < 0 || idx[j] >= p->num_slots) {
+        if (bad_request) *bad_request = b;
+        return TV_ERR_INPUT;
+      }
+    }
+  }
+  return TV_OK;
+}
+
+const char* tv_status_str(tv_status s) {
+  switch (s) {
+    case TV_OK: return "ok";
+    case TV_ERR_NULL: return "a required pointer is NULL";
+    case TV_ERR_SHAPE: return "a size in tv_problem is out of range or inconsistent";
+    case TV_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case TV_ERR_UNSUPPORTED: return "unsupported output dtype";
+    case TV_ERR_INPUT: return "device-side input violates a precondition";
+    case TV_ERR_LAUNCH: return "kernel launch failed (the library holds gfx950 code only)";
+    case TV_ERR_HIP: return "HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

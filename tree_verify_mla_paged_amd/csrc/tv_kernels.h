@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tv {
+
+constexpr int ROWS_PER_WG = 128;  // query rows (draft x head) per workgroup: 4 waves x 32
+constexpr int TILE_KEYS = 32;     // keys per LDS tile
+constexpr int SPLIT_STAGES = 3;   // LDS stages of the split kernel (stages-1 tiles in flight)
+constexpr int OUT_BF16 = 0;
+constexpr int OUT_F32 = 1;
+
+struct PackParams {
+  const uint8_t* mask;
+  const int32_t* mask_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* qo_indptr;
+  uint32_t* words;            // [total_q, max_tiles] visibility words
+  int32_t max_tiles;          // ceil(max_kv_len / 32)
+};
+
+struct SplitScalars {
+  float scale_log2;           // sm_scale * log2(e)
+  int32_t num_heads;
+  int32_t split_keys;         // keys per split, multiple of TILE_KEYS
+  int32_t max_splits;
+  int32_t row_blocks;
+  int32_t total_work;         // batch * max_splits * row_blocks
+  int32_t max_tiles;
+};
+
+struct SplitParams {
+  const uint16_t* q;          // bf16 [total_q, H, 576]
+  const uint16_t* kv;         // bf16 [num_slots, 576]
+  const int32_t* kv_indices;
+  const int32_t* kv_indptr;
+  const int32_t* qo_indptr;
+  const uint32_t* mask_words; // [total_q, max_tiles] from tv_pack_mask_kernel
+  void* out;                  // [total_q, H, 512] bf16 or fp32 (requests with one split)
+  float* lse;                 // [total_q, H]
+  float* ws_o;                // [total_q * H, max_splits, 512] fp32 partial outputs
+  float* ws_lse;              // [total_q * H, max_splits] fp32 partial lse (natural log)
+  SplitScalars s;
+  bool wide;                  // pool larger than 4 GiB: 64-bit gather addresses
+};
+
+struct MergeParams {
+  const int32_t* kv_indptr;
+  const int32_t* qo_indptr;
+  const float* ws_o;
+  const float* ws_lse;
+  void* out;
+  float* lse;
+  int32_t num_heads;
+  int32_t split_keys;
+  int32_t max_splits;
+};
+
+hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st);
+hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, hipStream_t st);
+
+}  // namespace tv
