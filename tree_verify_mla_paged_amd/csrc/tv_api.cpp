@@ -175,7 +175,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     mp.num_heads = p->num_heads;
     mp.split_keys = lay.plan.split_keys;
     mp.max_splits = lay.plan.max_splits;
-    const int64_t gx = ceil_div((int64_t)p->max_q_len * p->num_heads, 2);
+    const int64_t gx = (int64_t)p->max_q_len * p->num_heads;  // one row per workgroup
     if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, s) != hipSuccess)
       return TV_ERR_LAUNCH;
   }

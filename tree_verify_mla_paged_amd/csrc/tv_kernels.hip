@@ -29,12 +29,14 @@
 //    in VGPRs for the whole split.  In the 32x32 accumulator layout lane l holds
 //    row l % 32 and 16 of the 32 keys: the row max / sum is a 16-register
 //    reduction plus one exchange with lane l ^ 32.
-//  * O^T[d, row] += V^T[d, key] . P^T[key, row]: B = bf16 of those same 16
-//    probabilities (no LDS round trip); A = V^T read straight from the
-//    row-major tile with ds_read_b64_tr_b16 (within 16 lanes, output lane i
-//    element j comes from source lane 4j + i/4, element i%4: when source lane
-//    4j+q points at dims d0+4q.. of key j, lane i gets keys j=0..3 at dim d0+i).
-//    O^T stays in the 256 accumulator registers (AGPRs) for the whole split.
+//  * O^T[d, row] += V^T[d, key] . P^T[key, row] is split by value dims instead:
+//    wave w owns dims 128w..128w+127 of all 128 rows (16 accumulators, the 256
+//    AGPRs), so the V tile is read once per workgroup rather than once per
+//    wave.  The bf16 probabilities go through a small LDS buffer in exactly the
+//    MFMA B operand layout; A = V^T read straight from the row-major tile with
+//    ds_read_b64_tr_b16 (within 16 lanes, output lane i element j comes from
+//    source lane 4j + i/4, element i%4: when source lane 4j+q points at dims
+//    d0+4q.. of key j, lane i gets keys j=0..3 at dim d0+i).
 //  * Reference maximum without rescaling: a row's reference is fixed at the
 //    maximum of its first tile with a visible key (O and l are still exactly 0
 //    then).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32 sums and
@@ -62,8 +64,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr int QK = 576;
 constexpr int VD = 512;
 constexpr int TILE = TILE_KEYS;
-constexpr int ROW = 1280;                 // LDS bytes per key for latent dims 0..511
-constexpr int MAIN_BYTES = TILE * ROW;    // 40960
+constexpr int ROW = 1088;                 // LDS row pitch of a key's latent dims 0..511
+constexpr int MAIN_BYTES = 34816;         // 32 rows at ROW plus the largest key_shift, 256-aligned
 constexpr int ROPE_BYTES = TILE * 128;    // RoPE dims 512..575 of 32 keys
 constexpr int MASKW_BYTES = 4 * 64 * 4;   // 256 visibility words (one per draft)
 constexpr int STAGE = MAIN_BYTES + ROPE_BYTES + MASKW_BYTES;  // 46080
@@ -71,14 +73,15 @@ constexpr int NSTAGE = 3;
 constexpr int DMA_PER_TILE = 10;          // direct-to-LDS loads per wave per tile
 constexpr float TAU = 64.0f;              // log2 headroom of a probability over its reference
 
-// A key's 1024 latent bytes sit at key*ROW + key_shift(key).  With ROW a
-// multiple of 256 bytes the shift alone picks the banks: the 16 keys of a QK
-// read (same chunk) land on 16 distinct 16-byte bank groups, and the 4 keys of a
-// transposed PV read (64 contiguous bytes each) on 4 distinct 64-byte groups.
-// The shift is additive, so every read is a per-lane base plus an immediate.
-__host__ __device__ constexpr int key_shift(int key) {
-  return 64 * (key & 3) + 16 * ((key >> 2) & 3);
-}
+// A key's 1024 latent bytes sit at key*ROW + key_shift(key).  Modulo 256 bytes
+// (one pass over the banks) that is 64*(key & 3) + 16*((key >> 2) & 3): the 16
+// keys of a QK read (same chunk) land on 16 distinct 16-byte bank groups, and
+// the 4 keys of a transposed PV read (32 contiguous bytes each) on distinct
+// groups.  The shift is additive, so every read is a per-lane base plus an
+// immediate.
+__host__ __device__ constexpr int key_shift(int key) { return 16 * ((key >> 2) & 3); }
+static_assert(ROW % 256 == 64, "bank residues assume ROW = 64 mod 256");
+static_assert(31 * ROW + key_shift(31) + 1024 <= MAIN_BYTES && MAIN_BYTES % 256 == 0, "");
 // XOR swizzle of the 8 RoPE chunks inside a key's 128-byte RoPE row.
 __device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
 
@@ -140,13 +143,6 @@ struct SplitCtx {
 // Their completion is tracked explicitly with vmcnt instead (nothing else in
 // the tile loop is a vector memory op).  M0 holds the LDS address; the global
 // address is an SGPR base plus a 32-bit VGPR offset, or a 64-bit VGPR address.
-template <int LDS_IMM>
-__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t m0base) {
-  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0base), "i"(LDS_IMM)
-               : "m0");
-}
 __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -162,54 +158,100 @@ __device__ __forceinline__ void dma4_s(uint32_t voff, const void* sbase, uint32_
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
+// A loop-invariant per-lane offset, made opaque so it is recomputed where it is
+// used: hoisted out of the tile loop, each (offset + constant) would occupy a
+// register of its own instead of folding the constant into the instruction.
+__device__ __forceinline__ int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Slots of this wave's 8 keys (8*wave .. 8*wave+7) of tile t: wave-uniform
 // scalar loads, clamped to the split's last key.  Tiles past the split (the
 // loop runs a multiple of 3 tiles) therefore gather real, finite rows, and their
 // keys are masked off, so they contribute exactly 0.
 __device__ __forceinline__ void load_slots(int (&slot)[8], const SplitCtx& c, int t) {
   const int kt = c.kbeg + t * TILE + 8 * c.wave;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) slot[i] = c.idx[min(kt + i, c.kend - 1)];
+  const int last = c.kend - 1;
+  // written out: every index of slot[] must be a constant before loop
+  // unrolling, or the array is moved to memory
+  slot[0] = c.idx[min(kt + 0, last)];
+  slot[1] = c.idx[min(kt + 1, last)];
+  slot[2] = c.idx[min(kt + 2, last)];
+  slot[3] = c.idx[min(kt + 3, last)];
+  slot[4] = c.idx[min(kt + 4, last)];
+  slot[5] = c.idx[min(kt + 5, last)];
+  slot[6] = c.idx[min(kt + 6, last)];
+  slot[7] = c.idx[min(kt + 7, last)];
 }
 
-// Latent dims 0..511 of key 8*wave + I go to stage + (8*wave + I)*ROW +
-// key_shift(8*wave + I) = stage + [8*wave*ROW + 32*(wave & 1)] + LDS_IMM(I).
-template <int I>
-__device__ __forceinline__ void issue_main(const SplitCtx& c, const int (&slot)[8],
-                                           uint32_t m0base) {
-  constexpr int IMM = I * ROW + 64 * (I & 3) + 16 * (I >> 2);
-  dma16_s<IMM>(c.voff, c.kv + (int64_t)slot[I] * QK, m0base);
-  if constexpr (I + 1 < 8) issue_main<I + 1>(c, slot, m0base);
+__device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "m0");
 }
 
-// Direct-to-LDS gather of tile t into stage sb: DMA_PER_TILE loads per wave.
-// WIDE: the pool may exceed 4 GiB, so the RoPE gather (one slot per 8 lanes)
-// uses 64-bit per-lane addresses; otherwise a 32-bit offset from the pool base.
-template <bool WIDE>
-__device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], const SplitCtx& c,
-                                           int t) {
-  issue_main<0>(c, slot, lds_addr(sb) + 8 * c.wave * ROW + 32 * (c.wave & 1));
-  {
+// The DMA_PER_TILE direct-to-LDS gathers of one tile, one piece at a time.
+//   piece 0..7: latent dims 0..511 of key 8*wave + j, to stage + (8*wave + j)*ROW
+//               + key_shift(8*wave + j) = m0main + j*ROW + 16*(j >> 2);
+//   piece 8:    RoPE dims of the wave's 8 keys (one slot per 8 lanes);
+//   piece 9:    the visibility words of the tile (one per draft row).
+// WIDE: the pool may exceed 4 GiB, so the RoPE gather uses 64-bit per-lane
+// addresses; otherwise a 32-bit offset from the pool base.  The slots are
+// taken by reference to the caller's array (a pointer kept in a struct makes
+// the compiler move the array to memory).
+template <bool WIDE, int J>
+__device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)[8],
+                                             const SplitCtx& c, int t) {
+  if constexpr (J < 8) {
+    const uint32_t m0 = lds_addr(sb) + 8 * c.wave * ROW + 32 * (c.wave & 1) + J * ROW +
+                        16 * (J >> 2);
+    dma16_m0(c.voff, c.kv + (int64_t)slot[J] * QK, m0);
+  } else if constexpr (J == 8) {
     // recomputed every tile from an opaque copy of the lane id: a hoisted,
     // loop-invariant per-lane offset would be spilled, and its reload (a
     // vector memory op) would wait out the gathers just issued
     int lane = c.lane;
     asm volatile("" : "+v"(lane));
-    const int j = lane >> 3;  // key 8*wave + j, RoPE chunk slot lane & 7
-    int s = slot[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) s = (j == i) ? slot[i] : s;
-    const int pos = 8 * c.wave + j;
+    const int k = lane >> 3;  // key 8*wave + k, RoPE chunk slot lane & 7
+    // the per-lane choice among the 8 slots is made on opaque values: a select
+    // between loads of slot[] would be folded into a per-lane indexed load,
+    // which moves the whole array to memory
+    int s0 = slot[0], s1 = slot[1], s2 = slot[2], s3 = slot[3];
+    int s4 = slot[4], s5 = slot[5], s6 = slot[6], s7 = slot[7];
+    asm volatile("" : "+s"(s0), "+s"(s1), "+s"(s2), "+s"(s3), "+s"(s4), "+s"(s5), "+s"(s6),
+                 "+s"(s7));
+    const int s = k < 4 ? (k < 2 ? (k == 0 ? s0 : s1) : (k == 2 ? s2 : s3))
+                        : (k < 6 ? (k == 4 ? s4 : s5) : (k == 6 ? s6 : s7));
+    const int pos = 8 * c.wave + k;
     const uint32_t chunk = (uint32_t)((lane & 7) ^ rope_swz(pos));
     const uint32_t m0 = lds_addr(sb) + MAIN_BYTES + 8 * c.wave * 128;
     if constexpr (WIDE) {
       dma16_v(c.kv + (int64_t)s * QK + VD + chunk * 8, m0);
     } else {
-      dma16_s<0>((uint32_t)s * (QK * 2) + VD * 2 + chunk * 16, c.kv, m0);
+      dma16_m0((uint32_t)s * (QK * 2) + VD * 2 + chunk * 16, c.kv, m0);
     }
+  } else {
+    dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1),
+           lds_addr(sb) + MAIN_BYTES + ROPE_BYTES + 256 * c.wave);
   }
-  dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1),
-         lds_addr(sb) + MAIN_BYTES + ROPE_BYTES + 256 * c.wave);
+}
+
+template <bool WIDE>
+__device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], const SplitCtx& c,
+                                           int t) {
+  static_assert(DMA_PER_TILE == 10, "");
+  gather_piece<WIDE, 0>(sb, slot, c, t);
+  gather_piece<WIDE, 1>(sb, slot, c, t);
+  gather_piece<WIDE, 2>(sb, slot, c, t);
+  gather_piece<WIDE, 3>(sb, slot, c, t);
+  gather_piece<WIDE, 4>(sb, slot, c, t);
+  gather_piece<WIDE, 5>(sb, slot, c, t);
+  gather_piece<WIDE, 6>(sb, slot, c, t);
+  gather_piece<WIDE, 7>(sb, slot, c, t);
+  gather_piece<WIDE, 8>(sb, slot, c, t);
+  gather_piece<WIDE, 9>(sb, slot, c, t);
 }
 
 // The MFMAs of the tile loop are inline asm: S^T accumulates in VGPRs and O^T
@@ -236,9 +278,8 @@ __device__ __forceinline__ void mfma_drain_v(f32x16& acc) {
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int QK_AHEAD = 4;  // (>= 4: the RoPE B operands are read inside the chain)
-static_assert(true, "");  // LDS operand reads in flight ahead of the QK MFMA chain
-constexpr int PV_AHEAD = 4;  // ... and ahead of the PV MFMAs
+constexpr int QK_AHEAD = 4;  // LDS operand reads in flight ahead of the QK MFMA chain
+                             // (>= 4: the RoPE B operands are read inside the chain)
 
 // Q's 64 RoPE dims live in LDS (QR_ROW bytes per query row, padded so the 16
 // rows a QK read touches hit distinct banks); the 512 latent dims stay in VGPRs.
@@ -249,6 +290,7 @@ __device__ __forceinline__ f32x16 qk_tile(const lds_u8* sb, const lds_u8* qrope,
                                           const bf16x8 (&qf)[VD / 16], const SplitCtx& c) {
   constexpr int NK = QK / 16;  // 36 k-steps: 32 latent (B in VGPRs), 4 RoPE (B in LDS)
   const lds_u8* qa = sb + c.qk_off;
+  const lds_u8* qr = qrope + fresh(c.qr_off);
   auto a_addr = [&](int ks) -> const lds_u8* {
     return ks < VD / 16 ? qa + 32 * ks : sb + c.rp_off[ks - VD / 16];
   };
@@ -263,7 +305,7 @@ __device__ __forceinline__ f32x16 qk_tile(const lds_u8* sb, const lds_u8* qrope,
     if (nk < NK) {
       buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(nk));
       if (nk >= VD / 16)
-        bq[nk - VD / 16] = *reinterpret_cast<lds_bf16x8*>(qrope + c.qr_off + 32 * (nk - VD / 16));
+        bq[nk - VD / 16] = *reinterpret_cast<lds_bf16x8*>(qr + 32 * (nk - VD / 16));
     }
     const bf16x8 b = ks < VD / 16 ? qf[ks] : bq[ks - VD / 16];
     if (ks == 0) mfma_first_v(acc, a, b);
@@ -285,12 +327,14 @@ __device__ __forceinline__ uint32_t tile_mask(const lds_u8* sb, const SplitCtx& 
 // Masked, scaled scores (log2 units) of the lane's 16 keys and their row max.
 __device__ __forceinline__ float scores(float (&x)[16], const f32x16& acc, uint32_t mw,
                                         const SplitCtx& c) {
-  const int half = c.lane >> 5;
+  // register i holds key 8*(i/4) + 4*half + i%4: shift the half out once so
+  // every bit position below is a constant (per-lane masks would each hold a
+  // register for the whole loop)
+  const uint32_t mh = mw >> (4 * (c.lane >> 5));
   float tmax = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int pos = 8 * (i >> 2) + 4 * half + (i & 3);  // accumulator row of register i
-    x[i] = ((mw >> pos) & 1u) ? acc[i] * c.scale_log2 : -INFINITY;
+    x[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? acc[i] * c.scale_log2 : -INFINITY;
     tmax = fmaxf(tmax, x[i]);
   }
   return fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -305,19 +349,23 @@ __device__ __forceinline__ void tile_head(const SplitCtx& c, int t, int nt) {
   __syncthreads();
 }
 
-// Pipeline body of tile t in stage CUR: gather tile t+2 into stage (CUR+2)%3,
-// then consume tile t.  m_true tracks each row's maximum over all tiles; a
-// score above the row's reference by more than 2^TAU raises *flag (the pass is
-// then redone with the reference preset to m_true; this pass's accumulators,
+// Pipeline body of tile t (stage sb): gather tile t+2 into stage sg, then
+// consume tile t.  m_true tracks each row's maximum over all tiles; a score
+// above the row's reference by more than 2^TAU raises *flag (the pass is then
+// redone with the reference preset to m_true; this pass's accumulators,
 // possibly non-finite by then, are discarded).
-template <int CUR, bool WIDE>
-__device__ __forceinline__ void tile_body(lds_u8* const (&stages)[NSTAGE], int t, int nt,
+//
+// QK and the softmax are row-partitioned (wave w: rows 32w..32w+31); PV is
+// dim-partitioned (wave w: value dims 128w..128w+127 of all 128 rows), so each
+// wave reads a quarter of the V tile instead of all of it.  P^T moves between
+// the two through pbuf: [row block][k-step][lane] 16-byte MFMA B operands.
+template <bool WIDE>
+__device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, int nt,
                                           int (&slot)[8], const SplitCtx& c,
-                                          const lds_u8* qrope, const bf16x8 (&qf)[VD / 16],
-                                          f32x16 (&O)[VD / 32], float& m_ref, float& m_true,
-                                          float& l_sum, int* flag) {
-  if (t + 2 < nt) issue_tile<WIDE>(stages[(CUR + 2) % NSTAGE], slot, c, t + 2);
-  const lds_u8* sb = stages[CUR];
+                                          const lds_u8* qrope, lds_u8* pbuf,
+                                          const bf16x8 (&qf)[VD / 16], f32x16 (&O)[16],
+                                          float& m_ref, float& m_true, float& l_sum, int* flag) {
+  if (t + 2 < nt) issue_tile<WIDE>(sg, slot, c, t + 2);
   const uint32_t mw = tile_mask(sb, c, t);
   const f32x16 acc = qk_tile(sb, qrope, qf, c);
   float x[16];
@@ -333,11 +381,18 @@ __device__ __forceinline__ void tile_body(lds_u8* const (&stages)[NSTAGE], int t
     l_sum += e;
     pk[i >> 3][i & 7] = (__bf16)e;
   }
-  // O^T += V^T . P^T; k-step kst covers keys 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.
-  // MFMA m = 2*db + kst; its A operand is two transposed 8-byte reads.
+  // P^T of this wave's rows: register i of lane l is key 8*(i/4) + 4*(l/32) + i%4
+  // of row l%32, which is exactly the B operand layout of k-steps 0 (i < 8) and 1
+  *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + c.wave * 2048 +
+                                                               c.lane * 16) = pk[0];
+  *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + c.wave * 2048 + 1024 +
+                                                               c.lane * 16) = pk[1];
+  __syncthreads();  // P^T of all 128 rows is in pbuf
+  // O^T[dims of db, rows of rb] += V^T . P^T; k-step kst covers keys
+  // 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.  A operand (dim block db of
+  // this wave) = two transposed 8-byte reads; B operand (row block rb) = pbuf.
   const lds_u8* va = sb + c.pv_off;
-  auto pv_read = [&](int m) -> bf16x8 {
-    const int db = m >> 1, kst = m & 1;
+  auto pv_a = [&](int kst, int db) -> bf16x8 {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4*)(va + (16 * kst) * ROW + 64 * db));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -346,49 +401,76 @@ __device__ __forceinline__ void tile_body(lds_u8* const (&stages)[NSTAGE], int t
     const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
     return bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
   };
-  constexpr int NM = VD / 16;  // 32 MFMAs
-  bf16x8 vb[PV_AHEAD];
+  const lds_u8* pb = pbuf + fresh(c.lane * 16);
+  auto pv_b = [&](int kst, int rb) -> bf16x8 {
+    return *reinterpret_cast<lds_bf16x8*>(pb + rb * 2048 + kst * 1024);
+  };
+  // all 8 B operands stay live; the A operands of one dim block (both k-steps)
+  // are read while the previous block's 8 MFMAs run
+  bf16x8 B[2][4], A[2][2];
 #pragma unroll
-  for (int m = 0; m < PV_AHEAD; ++m) vb[m] = pv_read(m);
+  for (int i = 0; i < 4; ++i) B[0][i] = pv_b(0, i);
+  A[0][0] = pv_a(0, 0);
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const bf16x8 a = vb[m % PV_AHEAD];
-    if (m + PV_AHEAD < NM) vb[m % PV_AHEAD] = pv_read(m + PV_AHEAD);
-    mfma_acc_a(O[m >> 1], a, pk[m & 1]);
+  for (int i = 0; i < 4; ++i) B[1][i] = pv_b(1, i);
+  A[0][1] = pv_a(1, 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int cur = db & 1;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[cur][kst], B[kst][rb]);
+      if (db + 1 < 4) A[cur ^ 1][kst] = pv_a(kst, db + 1);
+    }
   }
   // slots of tile t+3, for the gather issued by the next tile's body; loaded
   // last so no scalar load is outstanding while the LDS reads above pipeline
   if (t + 3 < nt) load_slots(slot, c, t + 3);
 }
 
-// All tiles of the split (c.ntiles >= 1), padded to a multiple of 3 with
-// masked tiles; one exit, at the top (an exit between the tiles of a group
-// costs the register allocator dearly).  Returns true if a restart is needed;
-// every wave reads the flag after the same final barrier.
+// All tiles of the split (c.ntiles >= 1), one loop body: the stage of tile t
+// is chosen at run time (the gathers are inline asm, invisible to the
+// compiler's alias analysis, so a run-time stage costs no waits).  The code is
+// executed cold once per workgroup, so it is kept to one copy.  Returns true
+// if a restart is needed; every wave reads the flag after the same final
+// barrier.
 template <bool WIDE>
-__device__ __forceinline__ bool run_split(lds_u8* const (&stages)[NSTAGE], const SplitCtx& c,
-                                          const lds_u8* qrope, const bf16x8 (&qf)[VD / 16],
-                                          f32x16 (&O)[VD / 32], float& m_ref, float& m_true,
+__device__ __forceinline__ bool run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
+                                          lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
+                                          f32x16 (&O)[16], float& m_ref, float& m_true,
                                           float& l_sum, int* flag) {
-  const int nt = ((c.ntiles + NSTAGE - 1) / NSTAGE) * NSTAGE;
+  const int nt = c.ntiles;
   int slot[8];
   load_slots(slot, c, 0);
-  issue_tile<WIDE>(stages[0], slot, c, 0);
-  load_slots(slot, c, 1);
-  issue_tile<WIDE>(stages[1], slot, c, 1);
-  load_slots(slot, c, 2);
-  for (int t = 0; t < nt; t += NSTAGE) {
+  issue_tile<WIDE>(stages, slot, c, 0);
+  if (nt > 1) {
+    load_slots(slot, c, 1);
+    issue_tile<WIDE>(stages + STAGE, slot, c, 1);
+  }
+  if (nt > 2) load_slots(slot, c, 2);
+  int cur = 0;  // stage of tile t; tile t+2 goes to the stage of tile t-1
+  for (int t = 0; t < nt; ++t) {
     tile_head(c, t, nt);
-    tile_body<0, WIDE>(stages, t, nt, slot, c, qrope, qf, O, m_ref, m_true, l_sum, flag);
-    tile_head(c, t + 1, nt);
-    tile_body<1, WIDE>(stages, t + 1, nt, slot, c, qrope, qf, O, m_ref, m_true, l_sum, flag);
-    tile_head(c, t + 2, nt);
-    tile_body<2, WIDE>(stages, t + 2, nt, slot, c, qrope, qf, O, m_ref, m_true, l_sum, flag);
+    const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;
+    tile_body<WIDE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, slot, c, qrope, pbuf, qf,
+                    O, m_ref, m_true, l_sum, flag);
+    cur = cur == NSTAGE - 1 ? 0 : cur + 1;
   }
   // drain: no gather may still be writing a stage when another pass reuses it
   wait_vmcnt<0>();
   __syncthreads();
   return *flag != 0;
+}
+
+// O = 0 by MFMAs with zero operands: 16 instructions instead of 256
+// accumulator writes (this code, too, runs cold once per workgroup).
+__device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
+  bf16x8 z = bf16x8{};
+  asm volatile("" : "+v"(z));
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
 }
 
 template <int OUT, bool WIDE>
@@ -398,13 +480,14 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const int32_t* __restrict__ qo_indptr_, const uint32_t* __restrict__ mask_words_,
     void* __restrict__ out_, float* __restrict__ lse_, float* __restrict__ ws_o_,
     float* __restrict__ ws_lse_, SplitScalars p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t qrope_s[ROWS_PER_WG * QR_ROW];
+  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[4 * 2 * 64 * 16];
+  __shared__ float inv_s[ROWS_PER_WG];
   __shared__ int restart_flag;
-  lds_u8* const stages[NSTAGE] = {(lds_u8*)stage0, (lds_u8*)stage1, (lds_u8*)stage2};
+  lds_u8* const stages = (lds_u8*)stages_s;
   lds_u8* const qrope = (lds_u8*)qrope_s;
+  lds_u8* const pbuf = (lds_u8*)pbuf_s;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,11 +544,12 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     c.rp_off[j] = MAIN_BYTES + l32 * 128 + 16 * ((2 * j + half) ^ rope_swz(l32));
   // PV transposed reads: 16-lane group g16 = lane >> 4 picks dims +16*(g16 & 1);
   // source lane sl = lane & 15 points at key 4*half + sl/4, dims 4*(sl & 3)..+3.
-  // Key 16*kst + 8*rd + 4*half + sl/4, dims 32*db + 16*(g16 & 1) + 4*(sl & 3):
-  // pv_off + (16*kst + 8*rd)*ROW + 32*rd + 64*db  (key_shift is additive in rd)
+  // Key 16*kst + 8*rd + 4*half + sl/4, dims 128*wave + 32*db + 16*(g16 & 1) +
+  // 4*(sl & 3): pv_off + (16*kst + 8*rd)*ROW + 32*rd + 64*db, since
+  // key_shift(key) = 16*(2*rd + half) is additive in rd
   {
     const int sl = lane & 15;
-    c.pv_off = (4 * half + (sl >> 2)) * ROW + 64 * (sl >> 2) + 16 * half +
+    c.pv_off = (4 * half + (sl >> 2)) * ROW + 16 * half + 256 * wave +
                32 * ((lane >> 4) & 1) + 8 * (sl & 3);
   }
   c.mw_off = MAIN_BYTES + ROPE_BYTES + 4 * dl;
@@ -490,11 +574,18 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     }
   }
   c.qr_off = (wave * 32 + l32) * QR_ROW + 16 * half;  // + 32*j: RoPE chunk 2*j + half
+  // every Q load has landed before the tile loop (an asm use of each register
+  // makes the compiler wait here): otherwise it keeps the qf registers pending
+  // at the loop header and puts a vmcnt wait before each QK MFMA, which in
+  // steady state waits out the tile gathers instead
+#pragma unroll
+  for (int ks = 0; ks < VD / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
   __syncthreads();
 
-  f32x16 O[VD / 32];
-#pragma unroll
-  for (int i = 0; i < VD / 32; ++i) O[i] = f32x16{};
+  // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
+  // 4*(l/32) + r%4) and rows 32*rb + l%32: accumulator O[4*db + rb]
+  f32x16 O[16];
+  zero_acc(O);
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
   if (c.ntiles > 0) {
@@ -505,9 +596,9 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
       float m_true = -INFINITY;
       m_ref = m_pre;
       l_sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < VD / 32; ++i) O[i] = f32x16{};
-      if (!run_split<WIDE>(stages, c, qrope, qf, O, m_ref, m_true, l_sum, &restart_flag)) break;
+      if (pass > 0) zero_acc(O);
+      if (!run_split<WIDE>(stages, c, qrope, pbuf, qf, O, m_ref, m_true, l_sum, &restart_flag))
+        break;
       // a score exceeded its reference by more than 2^TAU: redo the split with
       // every row's reference at its true maximum (no score can exceed it)
       m_pre = m_true;
@@ -523,51 +614,60 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
                  "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
   const float l_tot = l_sum + __shfl_xor(l_sum, 32);
   const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
   // v_log_f32 is log2
   const float lse_nat = empty ? -INFINITY
                               : (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
-  if (!c.row_ok) return;
+  if (half == 0) inv_s[wave * 32 + l32] = empty ? 0.f : 1.f / l_tot;
+  if (c.row_ok && half == 0) {
+    if (nsplit == 1) lse_[g] = lse_nat;
+    else ws_lse_[g * p.max_splits + s] = lse_nat;
+  }
+  __syncthreads();
 
-  if (nsplit == 1) {
-    if (half == 0) lse_[g] = lse_nat;
+  // O^T -> LDS -> global, one row block (32 rows) at a time: wave w puts its
+  // 128 dims of the 32 rows into region w ([32 rows][EP_ROW bytes]); then each
+  // row is stored as one contiguous run by 128 threads (a small rolled loop:
+  // like the rest of the kernel this code runs cold once per workgroup).
+  constexpr int EP_ROW = 528;  // 512 bytes of a row's 128 dims, + 16: conflict-free writes
+  static_assert(4 * 32 * EP_ROW <= NSTAGE * STAGE, "");
+  {
+    lds_u8* ep = stages + wave * 32 * EP_ROW + l32 * EP_ROW + 16 * half;
+    const int64_t gb = (int64_t)q0 * H + row0;  // global row of the block's first row
+    const int d = 4 * (tid & 127);              // this thread's dims in the store loop
+    const lds_u8* rd = stages + (d >> 7) * 32 * EP_ROW + (d & 127) * 4;
 #pragma unroll
-    for (int db = 0; db < VD / 32; ++db) {
+    for (int rb = 0; rb < 4; ++rb) {
+      if (rb > 0) __syncthreads();  // the previous row block has been read back
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = db * 32 + 8 * rq + 4 * half;
-        f32x4 v;
-        v[0] = O[db][4 * rq + 0] * inv;
-        v[1] = O[db][4 * rq + 1] * inv;
-        v[2] = O[db][4 * rq + 2] * inv;
-        v[3] = O[db][4 * rq + 3] * inv;
-        if (OUT == OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + g * VD + d0) = v;
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& o = O[4 * db + rb];
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(ep + 128 * db + 32 * q) =
+              f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        }
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int i = 0; i < 16; ++i) {
+        const int lr = 2 * i + (tid >> 7);  // row within the row block
+        const int rl = 32 * rb + lr;        // row within the workgroup's block
+        if (row0 + rl >= R) break;
+        f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            rd + lr * EP_ROW);
+        v *= inv_s[rl];
+        if (nsplit > 1) {
+          *reinterpret_cast<f32x4*>(ws_o_ + ((gb + rl) * p.max_splits + s) * VD + d) = v;
+        } else if (OUT == OUT_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + (gb + rl) * VD + d) = v;
         } else {
           bf16x4 w;
           w[0] = (__bf16)v[0];
           w[1] = (__bf16)v[1];
           w[2] = (__bf16)v[2];
           w[3] = (__bf16)v[3];
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out_) + g * VD + d0) = w;
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out_) + (gb + rl) * VD + d) = w;
         }
-      }
-    }
-  } else {
-    const int64_t ps = g * p.max_splits + s;
-    if (half == 0) ws_lse_[ps] = lse_nat;
-    float* po = ws_o_ + ps * VD;
-#pragma unroll
-    for (int db = 0; db < VD / 32; ++db) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = db * 32 + 8 * rq + 4 * half;
-        f32x4 v;
-        v[0] = O[db][4 * rq + 0] * inv;
-        v[1] = O[db][4 * rq + 1] * inv;
-        v[2] = O[db][4 * rq + 2] * inv;
-        v[3] = O[db][4 * rq + 3] * inv;
-        *reinterpret_cast<f32x4*>(po + d0) = v;
       }
     }
   }
@@ -575,15 +675,18 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
 
 // ---------------------------------------------------------------- merge kernel
 
-// One row per 128 threads; each thread owns 4 consecutive value dims and
-// consumes the splits 8 at a time, so 8 independent loads are in flight.
+// One row per workgroup.  Thread t owns value dims 4*(t & 127) .. +3; the two
+// halves of the workgroup take alternate splits (8 loads in flight per thread)
+// and combine through LDS.
 template <int OUT>
 __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
   constexpr int U = 8;
+  __shared__ f32x4 part_o[128];
+  __shared__ float part_w[128];
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
   const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
-  const int r = blockIdx.x * 2 + (threadIdx.x >> 7);
+  const int r = blockIdx.x;
   if (r >= R) return;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
   const int ns = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
@@ -598,17 +701,19 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
 #pragma unroll
     for (int j = 0; j < U; ++j) M = fmaxf(M, v[j]);
   }
-  const int d = (threadIdx.x & 127) * 4;
+  const int t = threadIdx.x;
+  const int d = (t & 127) * 4;
+  const int h = t >> 7;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
     const float* po = p.ws_o + g * p.max_splits * VD + d;
-    for (int s0 = 0; s0 < ns; s0 += U) {
+    for (int s0 = h; s0 < ns; s0 += 2 * U) {
       float wgt[U];
       f32x4 v[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int s = s0 + j;
+        const int s = s0 + 2 * j;
         // exp(-inf) = 0 for an empty split, whose partial output is not read
         wgt[j] = s < ns ? expf(ls[s] - M) : 0.f;
         v[j] = wgt[j] > 0.f ? *reinterpret_cast<const f32x4*>(po + (int64_t)s * VD)
@@ -620,10 +725,18 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
         W += wgt[j];
       }
     }
-    acc *= 1.f / W;
   }
+  if (h == 1) {
+    part_o[t & 127] = acc;
+    part_w[t & 127] = W;
+  }
+  __syncthreads();
+  if (h == 1) return;
+  acc += part_o[t];
+  W += part_w[t];
+  if (M != -INFINITY) acc *= 1.f / W;
   const float lse = (M == -INFINITY) ? -INFINITY : M + logf(W);
-  if ((threadIdx.x & 127) == 0) p.lse[g] = lse;
+  if (t == 0) p.lse[g] = lse;
   if (OUT == OUT_F32) {
     *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + g * VD + d) = acc;
   } else {
