@@ -2,13 +2,19 @@
 """Benchmark of tree-masked verify attention on one MI355X.
 
 One step = one tv_verify_attn call (mask packing + split attention + LSE merge)
-over one batch of seeded synthetic inputs already resident in HBM, replayed from
-a captured HIP graph.  Default workload: 1 request, 32 draft tokens, 32768-key
-prefix, 16 heads (the 32k-prefix configuration the metric is quoted at).
+over one batch of seeded synthetic inputs already resident in HBM.  The timed
+steps are `steps` calls enqueued back to back on one stream, each with a HIP
+event pair around its split-attention kernel (events recorded inside a captured
+graph cannot be timed on this runtime); the same call replayed from a captured
+HIP graph is timed separately and reported beside it.  Default workload: 1 request, 32
+draft tokens, 32768-key prefix, 16 heads (the 32k-prefix configuration the
+metric is quoted at), with the library's own split plan (`--splits 32` gives
+the configuration's literal split count; outputs do not depend on it).
 
 Prints one JSON line: throughput as gathered-KV GB/s (sum over requests of
-L_b * 1152 bytes per call / call time), the roofline of the split kernel timed
-live with HIP events, and the fp64 CPU oracle timed on a bounded sample.
+L_b * 1152 bytes per call / call time), the roofline of the split kernel from
+its event-timed average over the timed steps, and the fp64 CPU oracle timed on
+a bounded sample.
 """
 import argparse
 import ctypes
@@ -90,22 +96,105 @@ def algorithmic(w):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("tv_kernels.hip", "tv_kernels.h", "tv_api.cpp"):
+    for f in ("tv_split.hip", "tv_kernels.h", "tv_api.cpp"):
         h.update(open(os.path.join(ROOT, "tree_verify_mla_paged_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: str, splits):
+def measured_traffic(cfg: str, splits: int, precise: bool):
     """HBM bytes per split-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "split_kernel_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    e = d.get("workloads", {}).get(str(cfg))
-    if not e or e.get("source_hash") != source_hash() or e.get("splits") != splits:
+    e = d.get("workloads", {}).get("%s/splits=%d/precise=%d" % (cfg, splits, int(precise)))
+    if not e or e.get("source_hash") != source_hash():
         return None
     return e.get("bytes_per_launch")
+
+
+COPY_BYTES = 256 * 1024 * 1024  # the calibration copy of the counter runs
+
+
+def counter_workload(args):
+    """For the two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE): a plain
+    elementwise copy of COPY_BYTES (its counter reading calibrates the counter
+    to bytes), then `--counter-workload` calls of the benchmark configuration."""
+    import torch
+    import tree_verify_mla_paged_amd as tv
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    w, _, cfg_splits = workload(args.config, poison=False)
+    splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in dict(
+        q=w.q.view(np.int16), kv=w.kv.view(np.int16), kv_indices=w.kv_indices,
+        kv_indptr=w.kv_indptr, qo_indptr=w.qo_indptr, mask=w.mask,
+        mask_indptr=w.mask_indptr).items()}
+    p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
+                        int(w.kv_indices.size), int(w.mask.size), splits,
+                        tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
+                        tv.FLAG_PRECISE_P if args.precise else 0)
+    out = torch.empty((w.total_q, w.num_heads, 512),
+                      dtype=torch.float32 if args.out_f32 else torch.bfloat16, device="cuda")
+    lse = torch.empty((w.total_q, w.num_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(tv.workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    for _ in range(args.counter_workload):
+        tv.verify_attn(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                       t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws, ws.numel())
+    torch.cuda.synchronize()
+    print("counter workload: config %s, splits %d, %d calls" % (args.config, splits,
+                                                             args.counter_workload))
+
+
+def write_traffic(args):
+    """profiles/split_kernel_hbm_traffic.json from the two counter csv files:
+    per split-kernel dispatch, FETCH_SIZE and WRITE_SIZE (KiB) each scaled by
+    COPY_BYTES / (the same counter's reading for the calibration copy)."""
+    import csv
+    fetch_csv, write_csv = args.write_traffic
+    res = {}
+    for f, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        vals = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        copy = [v for k, v in vals.items() if "elementwise" in k and "MulFunctor" in k]
+        split = [v for k, v in vals.items() if "tv_split_kernel" in k]
+        if len(copy) != 1 or len(split) != 1:
+            raise SystemExit("%s: expected one copy and one split kernel, found %s"
+                             % (f, sorted(vals)))
+        copy_kib = float(np.mean(copy[0]))
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        split_kib = float(np.mean(split[0]))
+        res[counter] = {"copy_kernel_kib": copy_kib, "factor": factor,
+                        "split_kernel_kib_per_dispatch": split_kib, "dispatches": len(split[0]),
+                        "bytes_per_launch": split_kib * 1024.0 * factor}
+    path = os.path.join(ROOT, "profiles", "split_kernel_hbm_traffic.json")
+    d = json.load(open(path)) if os.path.exists(path) else {}
+    d["note"] = ("HBM bytes per tv_split_kernel dispatch: rocprofv3 --pmc FETCH_SIZE and "
+                 "WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the same "
+                 "counter read %d bytes for a plain copy of that size in the same run "
+                 "(bench.py --counter-workload)." % COPY_BYTES)
+    splits = args.splits if args.splits >= 0 else (workload(args.config, False)[2] or 0)
+    key = "%s/splits=%d/precise=%d" % (args.config, splits, int(args.precise))
+    d.setdefault("workloads", {})[key] = {
+        "source_hash": source_hash(),
+        "commands": ["rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py "
+                     "--config %s --splits %d%s --counter-workload %d" % (
+                         args.config, splits, " --precise" if args.precise else "", 10),
+                     "the same with --pmc WRITE_SIZE -o write",
+                     "python3 bench.py --config %s --splits %d%s --write-traffic "
+                     "<dir>/fetch_counter_collection.csv <dir>/write_counter_collection.csv" % (
+                         args.config, splits, " --precise" if args.precise else "")],
+        "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+        "bytes_per_launch": res["FETCH_SIZE"]["bytes_per_launch"] +
+        res["WRITE_SIZE"]["bytes_per_launch"]}
+    json.dump(d, open(path, "w"), indent=1)
+    print(json.dumps(d["workloads"][key], indent=1))
 
 
 def cpu_baseline(w, gpu_out, gpu_lse, kv_bytes, budget_s, out_f32):
@@ -155,18 +244,32 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="3", help="1-5 (benchmark configurations) or S1-S3")
-    ap.add_argument("--splits", type=int, default=-1,
-                    help="KV split count (0 = library heuristic; default: the configuration's own "
-                         "split count if it names one, else the heuristic)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="KV split count (0 = the library's plan; -1 = the configuration's own "
+                         "split count if it names one)")
     ap.add_argument("--out-f32", action="store_true")
+    ap.add_argument("--precise", action="store_true",
+                    help="probabilities as a bf16 hi + lo pair in the P.V product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--counter-workload", type=int, default=0, metavar="N",
+                    help="run the calibration copy and N calls for rocprofv3 --pmc, no timing")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise the two counter runs into profiles/ (no GPU needed)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (requests and heads "
-              "shard with no exchange; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU and has no multi-GPU path (requests and heads would "
+              "shard across GPUs with no exchange between them).  Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
+
+    if args.counter_workload > 0:
+        counter_workload(args)
+        return
 
     import torch
     import tree_verify_mla_paged_amd as tv
@@ -180,7 +283,8 @@ def main():
         mask_indptr=w.mask_indptr).items()}
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
-                        tv.OUT_F32 if args.out_f32 else tv.OUT_BF16)
+                        tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
+                        tv.FLAG_PRECISE_P if args.precise else 0)
     plan = tv.plan(p)
     N, H = w.total_q, w.num_heads
     out = torch.empty((N, H, 512), dtype=torch.float32 if args.out_f32 else torch.bfloat16,
@@ -191,53 +295,54 @@ def main():
     stream = torch.cuda.Stream()
     sid = int(stream.cuda_stream)
 
-    def call():
-        tv.verify_attn(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
-                       t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws, ws.numel(),
-                       stream=sid)
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def call(i=None):
+        if i is None:
+            tv.verify_attn(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                           t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws,
+                           ws.numel(), stream=sid)
+        else:
+            tv.verify_attn_timed(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"],
+                                 t["qo_indptr"], t["mask"], t["mask_indptr"], float(w.sm_scale),
+                                 out, lse, ws, ws.numel(), pairs[i][0], pairs[i][1], stream=sid)
 
     with torch.cuda.stream(stream):
         for _ in range(3):
             call()
     torch.cuda.synchronize()
+    # warmup steps
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    # the timed steps
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    split_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    split_avg_ms = float(np.mean(split_ms))
+
+    # the same call replayed from a captured graph (reported, not the metric)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         call()
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    for _ in range(5):
         graph.replay()
     torch.cuda.synchronize()
-
-    # timed region: exactly `steps` graph replays
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    g0 = time.perf_counter()
     for _ in range(args.steps):
         graph.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # the split kernel alone, timed with HIP events on its own stream
-    ev = HipEvents()
-    nrep = max(20, min(args.steps, 200))
-    pairs = [(ev.create(), ev.create()) for _ in range(nrep)]
-    whole0, whole1 = ev.create(), ev.create()
-    torch.cuda.synchronize()
-    ev.record(whole0, sid)
-    for a, b in pairs:
-        tv.verify_attn_timed(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
-                             t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws,
-                             ws.numel(), a, b, stream=sid)
-    ev.record(whole1, sid)
-    torch.cuda.synchronize()
-    split_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    eager_ms = ev.elapsed_ms(whole0, whole1) / nrep
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
-    ev.destroy(whole0)
-    ev.destroy(whole1)
-    split_avg_ms = float(np.mean(split_ms))
+    graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
 
     kv_bytes, total_bytes, flops = algorithmic(w)
     us_per_call = ms_per_step * 1e3
@@ -252,7 +357,7 @@ def main():
         achieved = total_bytes / (split_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-    roof["traffic"] = measured_traffic(args.config, splits)
+    roof["traffic"] = measured_traffic(args.config, splits, bool(args.precise))
     roof["kernel"] = "tv_split_kernel"
     roof["kernel_avg_us"] = split_avg_ms * 1e3
     roof["algorithmic"] = {"bytes": total_bytes, "flops": flops,
@@ -264,11 +369,12 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, bf16-rounded N(0,1))",
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
-        "eager_us_per_call": eager_ms * 1e3,
+        "graph_us_per_call": graph_us,
         "floor_fraction": max(t_hbm, t_mfma) / (ms_per_step * 1e-3),
         "config": {"workload": desc, "requests": w.batch, "n_draft": int(w.max_q_len),
                    "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,
                    "plan": plan, "out_dtype": "f32" if args.out_f32 else "bf16",
+                   "precise_p": bool(args.precise),
                    "gathered_kv_bytes": kv_bytes, "visible_pairs_x_heads": w.visible_pairs() * H},
         "roofline": roof,
     }

@@ -48,13 +48,22 @@ typedef enum {
   TV_ERR_NULL = 1,        /* a required pointer is NULL                                  */
   TV_ERR_SHAPE = 2,       /* a size in tv_problem is out of range or inconsistent        */
   TV_ERR_WORKSPACE = 3,   /* workspace is NULL or smaller than tv_workspace_bytes()      */
-  TV_ERR_UNSUPPORTED = 4, /* out_dtype unknown                                           */
+  TV_ERR_UNSUPPORTED = 4, /* out_dtype or a flags bit unknown, reserved != 0             */
   TV_ERR_INPUT = 5,       /* tv_check_inputs found a device-side precondition violated   */
   TV_ERR_LAUNCH = 6,      /* a kernel launch failed (e.g. the current device is not gfx950) */
   TV_ERR_HIP = 7          /* a HIP runtime call inside tv_check_inputs failed            */
 } tv_status;
 
 typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
+
+/* tv_problem.flags.  The softmax probabilities (fp32) enter the P.V product on
+ * the bf16 matrix cores.  By default each is rounded once to bf16, which bounds
+ * the output error by 2^-9 * max |v| over the row's visible keys.
+ * TV_FLAG_PRECISE_P splits each probability into two bf16 terms (hi + lo, about
+ * 16 significant bits) and runs the P.V product on both: the error bound
+ * becomes about 2^-17 * max |v| for 32 more MFMAs per 32-key tile (68 -> 100).
+ * Meant for value distributions with large outliers. */
+#define TV_FLAG_PRECISE_P 1
 
 /* Host-side description of one call.  Device-side lengths may vary between
  * calls (or graph replays) as long as they stay within these bounds. */
@@ -73,6 +82,8 @@ typedef struct tv_problem {
                          rounded up to the 32-key tile; shorter requests use as
                          many splits of that size as they need                      */
   int32_t out_dtype;  /* tv_out_dtype                                                */
+  int32_t flags;      /* TV_FLAG_* bits; unknown bits -> TV_ERR_UNSUPPORTED           */
+  int32_t reserved;   /* must be 0                                                   */
 } tv_problem;
 
 /* Launch plan that tv_verify_attn uses for `p` (host arithmetic only). */

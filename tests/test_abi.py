@@ -86,9 +86,17 @@ def test_bad_shapes_are_rejected():
         with pytest.raises(tv.TreeVerifyError) as e:
             tv.plan(prob(**kw))
         assert e.value.code == 2
+    for kw in [dict(out_dtype=7), dict(flags=2), dict(flags=-1)]:
+        with pytest.raises(tv.TreeVerifyError) as e:
+            tv.plan(prob(**kw))
+        assert e.value.code == 4
+    bad = prob()
+    bad.reserved = 1
     with pytest.raises(tv.TreeVerifyError) as e:
-        tv.plan(prob(out_dtype=7))
+        tv.plan(bad)
     assert e.value.code == 4
+    # the precise-probability flag changes no plan or workspace arithmetic
+    assert tv.plan(prob(flags=tv.FLAG_PRECISE_P)) == tv.plan(prob())
 
 
 def test_null_pointers_and_short_workspace_fail_before_any_launch():
@@ -123,7 +131,8 @@ def test_check_inputs_validates_host_arguments_first():
 
 
 def test_problem_struct_layout_matches_header():
-    # int32, int32, int64, int32, int32, int64, int64, int64, int32, int32
-    assert ctypes.sizeof(tv.Problem) == 56
+    # int32, int32, int64, int32, int32, int64, int64, int64, int32, int32, int32, int32
+    assert ctypes.sizeof(tv.Problem) == 64
     assert tv.Problem.num_splits.offset == 48 and tv.Problem.out_dtype.offset == 52
+    assert tv.Problem.flags.offset == 56 and tv.Problem.reserved.offset == 60
     assert ctypes.sizeof(tv.Plan) == 24

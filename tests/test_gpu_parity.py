@@ -1,18 +1,27 @@
 """Parity of the HIP path (called through the C ABI) against the fp64 oracle.
 
 Bar (floating point): max |out - oracle| <= 8e-3 and sum|diff| / sum|oracle| <=
-2e-3 on bf16-rounded inputs; a bf16 output may additionally differ by half a
-bf16 ulp of the reference where |o| >= 2 (its own rounding).  lse: derived from
-fp32 accumulation of 576-term scores, |diff| <= 2e-4 * max(1, |lse|).
-Visibility handling is checked exactly (same visible-key set per row) and
-results are checked to be independent of the split count (lse within 1e-5).
+2e-3 on bf16-rounded inputs; a bf16 output may additionally differ by its own
+rounding (half a bf16 ulp per element; in the mean relative error, that of the
+reference rounded to bf16).  lse: derived from fp32
+accumulation of 576-term scores, |diff| <= 2e-4 * max(1, |lse|).
+
+The probabilities enter the P.V product as bf16.  Rounded once (the default),
+they move an output by at most 2^-9 * max|v_d| (gpu_util.p_rounding_bound):
+with N(0,1) values that stays under the bar, with the x30 outliers of the
+large-batch config it does not, and that config is held to the bar with the
+precise-probability flag (hi + lo pair, bound ~2^-17 * max|v_d|) and to the
+derived bound without it.  Visibility handling is checked exactly (same
+visible-key set per row) and results are checked to be independent of the
+split count: lse within 1e-5 in either mode, outputs within twice the
+rounding bound.
 """
 import numpy as np
 import pytest
 
 import oracle
 import tv_workload as W
-from gpu_util import GpuCall, compare, run, sample_rows, upload
+from gpu_util import GpuCall, compare, p_rounding_bound, run, sample_rows, upload
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -23,20 +32,22 @@ if not torch.cuda.is_available():
 import tree_verify_mla_paged_amd as tv  # noqa: E402  (fails loudly if the library is missing)
 
 
-def full_check(w, num_splits=0, out_f32=False, label=""):
+PRECISE = tv.FLAG_PRECISE_P
+
+
+def full_check(w, num_splits=0, out_f32=False, label="", flags=0, **kw):
     ro, rl = oracle.run(w)
-    o, l = run(w, num_splits=num_splits, out_f32=out_f32)
-    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label)
+    o, l = run(w, num_splits=num_splits, out_f32=out_f32, flags=flags)
+    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label, **kw)
 
 
-def sampled_check(w, nrows, num_splits=0, out_f32=False, label="", seed=0):
+def sampled_check(w, nrows, num_splits=0, out_f32=False, label="", seed=0, flags=0, **kw):
     rows = sample_rows(w, nrows, seed)
     ro, rl = oracle.run(w, rows=rows)
-    o, l = run(w, num_splits=num_splits, out_f32=out_f32)
-    H = w.num_heads
+    o, l = run(w, num_splits=num_splits, out_f32=out_f32, flags=flags)
     o = o.reshape(-1, 512)[rows]
     l = l.reshape(-1)[rows]
-    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label)
+    return compare(o, l, ro, rl, bf16_out=not out_f32, label=label, **kw)
 
 
 # ------------------------------------------------------------- the configs
@@ -66,8 +77,18 @@ def test_c4_200k_prefix():
 
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_c5_large_batch_with_outliers(out_f32):
-    print("C5 out_f32=%s" % out_f32, flush=True)
-    sampled_check(W.config(5), 96, out_f32=out_f32, label="C5")
+    """The x30 outliers: the bar with the precise-probability flag."""
+    print("C5 precise out_f32=%s" % out_f32, flush=True)
+    sampled_check(W.config(5), 96, out_f32=out_f32, label="C5 precise", flags=PRECISE)
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_c5_default_mode_within_rounding_bound(out_f32):
+    """Without the flag: the bar widened by the derived probability-rounding bound."""
+    print("C5 default out_f32=%s" % out_f32, flush=True)
+    w = W.config(5)
+    sampled_check(w, 96, out_f32=out_f32, label="C5 default",
+                  extra_abs=p_rounding_bound(w, precise=False))
 
 
 def test_long_prefix_live_shape():
@@ -95,10 +116,11 @@ SMALL = [
 
 @pytest.mark.parametrize("seed,prefix,ndraft,H,ns", SMALL)
 @pytest.mark.parametrize("out_f32", [False, True])
-def test_small_shapes(seed, prefix, ndraft, H, ns, out_f32):
-    print("small seed=%d H=%d ns=%d f32=%s" % (seed, H, ns, out_f32), flush=True)
+@pytest.mark.parametrize("flags", [0, 1])
+def test_small_shapes(seed, prefix, ndraft, H, ns, out_f32, flags):
+    print("small seed=%d H=%d ns=%d f32=%s flags=%d" % (seed, H, ns, out_f32, flags), flush=True)
     w = W.small(seed, prefix, ndraft, num_heads=H)
-    full_check(w, num_splits=ns, out_f32=out_f32, label="small%d" % seed)
+    full_check(w, num_splits=ns, out_f32=out_f32, label="small%d" % seed, flags=flags)
 
 
 def test_random_masks_many_splits():
@@ -115,13 +137,18 @@ def test_random_masks_many_splits():
 
 # ------------------------------------------------- split-count invariance
 
-def test_split_count_invariance():
+@pytest.mark.parametrize("flags", [0, 1])
+def test_split_count_invariance(flags):
+    """lse within 1e-5 for every split count; outputs within twice the bound on
+    the probability rounding (each run is within it of the exact result) plus
+    1e-5 for fp32 accumulation order."""
     w = W.config(3)
     rows = sample_rows(w, 64, seed=3)
+    tol_o = 2 * p_rounding_bound(w, precise=bool(flags)) + 1e-5
     ref_o = ref_l = None
     for ns in (1, 2, 3, 7, 16, 32, 64, 128):
-        print("C3 split invariance ns=%d" % ns, flush=True)
-        g = GpuCall(w, num_splits=ns, out_f32=True)
+        print("C3 split invariance ns=%d flags=%d" % (ns, flags), flush=True)
+        g = GpuCall(w, num_splits=ns, out_f32=True, flags=flags)
         g.call()
         o, l = g.result()
         o = o.reshape(-1, 512)
@@ -131,8 +158,11 @@ def test_split_count_invariance():
             ro, rl = oracle.run(w, rows=rows)
             compare(o[rows], l[rows], ro, rl, bf16_out=False, label="C3 ns=1")
             continue
-        assert np.abs(l - ref_l).max() <= 1e-5, ns
-        assert np.abs(o - ref_o).max() <= 1e-4, ns
+        dl = float(np.abs(l - ref_l).max())
+        do = np.abs(o - ref_o)
+        print("   max |dlse| %.3g  max |dout| %.3g" % (dl, float(do.max())), flush=True)
+        assert dl <= 1e-5, ns
+        assert (do <= tol_o).all(), ns
 
 
 # ------------------------------------------------------ exact visibility

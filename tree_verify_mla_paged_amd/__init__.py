@@ -17,6 +17,7 @@ QK_DIM = 576
 V_DIM = 512
 OUT_BF16 = 0
 OUT_F32 = 1
+FLAG_PRECISE_P = 1  # probabilities as a bf16 hi + lo pair in the P.V product
 
 STATUS = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_WORKSPACE",
           4: "TV_ERR_UNSUPPORTED", 5: "TV_ERR_INPUT", 6: "TV_ERR_LAUNCH", 7: "TV_ERR_HIP"}
@@ -31,7 +32,8 @@ class Problem(ctypes.Structure):
                 ("total_q", ctypes.c_int64), ("max_q_len", ctypes.c_int32),
                 ("max_kv_len", ctypes.c_int32), ("num_slots", ctypes.c_int64),
                 ("total_kv", ctypes.c_int64), ("total_mask", ctypes.c_int64),
-                ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -102,9 +104,9 @@ def _stream(stream) -> int:
 
 def make_problem(batch: int, num_heads: int, total_q: int, max_q_len: int, max_kv_len: int,
                  num_slots: int, total_kv: int, total_mask: int, num_splits: int = 0,
-                 out_dtype: int = OUT_BF16) -> Problem:
+                 out_dtype: int = OUT_BF16, flags: int = 0) -> Problem:
     return Problem(batch, num_heads, total_q, max_q_len, max_kv_len, num_slots, total_kv,
-                   total_mask, num_splits, out_dtype)
+                   total_mask, num_splits, out_dtype, flags, 0)
 
 
 def plan(problem: Problem) -> dict:

@@ -20,8 +20,9 @@
 #include "tv_kernels.h"
 #include "treeverify.h"
 
-static_assert(sizeof(tv_problem) == 56 && offsetof(tv_problem, total_q) == 8 &&
-                  offsetof(tv_problem, num_slots) == 24 && offsetof(tv_problem, out_dtype) == 52,
+static_assert(sizeof(tv_problem) == 64 && offsetof(tv_problem, total_q) == 8 &&
+                  offsetof(tv_problem, num_slots) == 24 && offsetof(tv_problem, out_dtype) == 52 &&
+                  offsetof(tv_problem, flags) == 56,
               "tv_problem layout is part of the ABI");
 static_assert(sizeof(tv_plan) == 24 && offsetof(tv_plan, workspace_bytes) == 16,
               "tv_plan layout is part of the ABI");
@@ -54,6 +55,7 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL)
     return TV_ERR_SHAPE;
   if (p->out_dtype != TV_OUT_BF16 && p->out_dtype != TV_OUT_F32) return TV_ERR_UNSUPPORTED;
+  if ((p->flags & ~TV_FLAG_PRECISE_P) != 0 || p->reserved != 0) return TV_ERR_UNSUPPORTED;
   if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
   if ((int64_t)p->max_q_len * p->num_heads > kMaxInt32 ||
       p->total_q * (int64_t)p->num_heads > kMaxInt32)
@@ -159,6 +161,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.s.total_work = (int32_t)((int64_t)p->batch * lay.plan.max_splits * lay.plan.row_blocks);
   sp.s.max_tiles = lay.max_tiles;
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
+  sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
   const int grid = (int)ceil_div(sp.s.total_work, 8) * 8;
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return TV_ERR_LAUNCH;
   if (tv::launch_split(sp, grid, p->out_dtype, s) != hipSuccess) return TV_ERR_LAUNCH;

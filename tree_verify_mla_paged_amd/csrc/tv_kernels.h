@@ -5,9 +5,17 @@
 
 namespace tv {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int QK = 576;           // key / query dims (512 latent + 64 RoPE)
+constexpr int VD = 512;           // value dims
 constexpr int ROWS_PER_WG = 128;  // query rows (draft x head) per workgroup: 4 waves x 32
 constexpr int TILE_KEYS = 32;     // keys per LDS tile
-constexpr int SPLIT_STAGES = 3;   // LDS stages of the split kernel (stages-1 tiles in flight)
 constexpr int OUT_BF16 = 0;
 constexpr int OUT_F32 = 1;
 
@@ -43,6 +51,7 @@ struct SplitParams {
   float* ws_lse;              // [total_q * H, max_splits] fp32 partial lse (natural log)
   SplitScalars s;
   bool wide;                  // pool larger than 4 GiB: 64-bit gather addresses
+  bool precise;               // probabilities as bf16 hi + lo in the P.V product
 };
 
 struct MergeParams {

@@ -1,29 +1,29 @@
-// Tree-masked verify attention over a paged MLA latent KV pool: gfx950 kernels.
+// Tree-masked verify attention over a paged MLA latent KV pool: the split
+// attention kernel for gfx950.
 //
 // Computation (page 3 "The Pivot to Live Cutover", sections "The Technical
 // Investigation" and "Input Knowledge Required"; page 2 "Flipping the Switch",
 // section "The Long Road to Parity"): for every draft row (token t, head h) of
 // request b, softmax over the visible gathered latent rows of sm_scale * q.k
 // (576 dims), applied to the first 512 dims of those rows, plus the natural
-// log-sum-exp.  Visibility is one mask byte per (draft, key), row stride L_b.
+// log-sum-exp.  Visibility is one mask byte per (draft, key), row stride L_b,
+// packed beforehand into one 32-bit word per (draft, 32-key tile).
 //
 // Method: KV-split flash decoding with an LSE merge (page 2, section "The
-// Broader Context").  Three kernels:
-//   tv_pack_mask_kernel  mask bytes -> one 32-bit visibility word per
-//                        (draft, 32-key tile), via wave ballots;
-//   tv_split_kernel      one (request, 128-row block, KV split) per workgroup;
-//   tv_merge_kernel      combines the splits of each row by their LSE.
+// Broader Context").  One workgroup per (request, 128-row block, KV split);
+// with more than one split it writes a normalised partial output and its LSE,
+// which tv_merge_kernel combines.
 //
-// gfx950 mapping of tv_split_kernel
+// gfx950 mapping
 //  * 4 wave64s; wave w owns 32 query rows (rows of a request are (draft, head)
 //    pairs, head fastest).  All 128 rows share each 32-key tile in LDS.
 //  * Tiles are gathered by direct-to-LDS 16-byte loads (global_load_lds_dwordx4):
 //    one instruction moves the 1024 bytes of a key's latent dims 0..511, one more
 //    per wave moves the 64 RoPE dims of 8 keys, one moves the visibility words.
-//    No registers hold in-flight tile data; three LDS stages (three distinct
-//    __shared__ objects, the tile loop unrolled by three so every access names
-//    its stage statically) keep two tiles in flight, and the compiler can see
-//    that reads of one stage never wait for the gathers into another.
+//    No registers hold in-flight tile data; three LDS stages keep two tiles in
+//    flight.  The gathers are inline asm tracked with explicit vmcnt waits, so
+//    the compiler sees no aliasing between them and the LDS reads, and the tile
+//    loop is one body with a run-time stage.
 //  * S^T[key, row] = K[key, :] . Q[row, :] with v_mfma_f32_32x32x16_bf16:
 //    A = key rows read from LDS (ds_read_b128), B = the wave's query rows held
 //    in VGPRs for the whole split.  In the 32x32 accumulator layout lane l holds
@@ -42,9 +42,12 @@
 //    then).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32 sums and
 //    bf16 operands hold exactly in range, so O is never rescaled in the loop and
 //    no VALU work ever touches the accumulators.  If some row's score exceeds
-//    its reference by more than TAU, the workgroup restarts the split once with
-//    each row's reference preset to its true maximum over the split (a QK-only
-//    pass), after which probabilities are <= 1.
+//    its reference by more than TAU, the workgroup runs the split again with
+//    each row's reference preset to its true maximum over the split (tracked
+//    during the first pass), after which probabilities are <= 1.
+//  * The kernel's straight-line code runs cold once per workgroup (instruction
+//    fetch), so prologue, loop and epilogue are kept compact: accumulators are
+//    zeroed by MFMAs, the epilogue is a rolled loop over LDS-staged rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,17 +55,7 @@
 
 namespace tv {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-#define GLB_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
-
-constexpr int QK = 576;
-constexpr int VD = 512;
 constexpr int TILE = TILE_KEYS;
 constexpr int ROW = 1088;                 // LDS row pitch of a key's latent dims 0..511
 constexpr int MAIN_BYTES = 34816;         // 32 rows at ROW plus the largest key_shift, 256-aligned
@@ -89,34 +82,6 @@ __device__ __forceinline__ int rope_swz(int key) { return (key >> 1) & 7; }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
-}
-
-// ---------------------------------------------------------------- mask packing
-
-// Word (token qo_indptr[b] + i, tile) bit k = mask byte of key 32*tile + k of draft i.
-// Each half-wave (32 lanes) builds one word; keys at or past L_b give 0.
-__global__ __launch_bounds__(256) void tv_pack_mask_kernel(PackParams p) {
-  const int b = blockIdx.y;
-  const int q0 = p.qo_indptr[b];
-  const int n = p.qo_indptr[b + 1] - q0;
-  const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
-  const int tiles = (L + TILE - 1) / TILE;
-  const int words = n * tiles;
-  const int w = blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int k = threadIdx.x & 31;
-  bool vis = false;
-  int i = 0, tile = 0;
-  if (w < words) {
-    i = w / tiles;
-    tile = w - i * tiles;
-    const int key = tile * TILE + k;
-    if (key < L) vis = p.mask[p.mask_indptr[b] + (int64_t)i * L + key] != 0;
-  }
-  const uint64_t bits = __ballot(vis);
-  if (w < words && k == 0) {
-    const uint32_t word = (threadIdx.x & 32) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
-    p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = word;
-  }
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -278,6 +243,7 @@ __device__ __forceinline__ void mfma_drain_v(f32x16& acc) {
 typedef const __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+constexpr int PBUF_LO = 4 * 2 * 64 * 16;  // bytes of P^T operands per tile (hi; lo follows)
 constexpr int QK_AHEAD = 4;  // LDS operand reads in flight ahead of the QK MFMA chain
                              // (>= 4: the RoPE B operands are read inside the chain)
 
@@ -359,7 +325,7 @@ __device__ __forceinline__ void tile_head(const SplitCtx& c, int t, int nt) {
 // dim-partitioned (wave w: value dims 128w..128w+127 of all 128 rows), so each
 // wave reads a quarter of the V tile instead of all of it.  P^T moves between
 // the two through pbuf: [row block][k-step][lane] 16-byte MFMA B operands.
-template <bool WIDE>
+template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, int nt,
                                           int (&slot)[8], const SplitCtx& c,
                                           const lds_u8* qrope, lds_u8* pbuf,
@@ -374,12 +340,15 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
   if (m_ref == -INFINITY) m_ref = tmax;  // first visible keys: O and l are still 0
   if (__any(tmax > m_ref + TAU) && c.lane == 0) *flag = 1;
   const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-  bf16x8 pk[2];
+  bf16x8 pk[2], pl[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float e = __builtin_amdgcn_exp2f(x[i] - mu);
     l_sum += e;
     pk[i >> 3][i & 7] = (__bf16)e;
+    // PRECISE: the rounding residual, itself rounded to bf16 (hi + lo carries
+    // about 16 significant bits of e)
+    if (PRECISE) pl[i >> 3][i & 7] = (__bf16)(e - (float)pk[i >> 3][i & 7]);
   }
   // P^T of this wave's rows: register i of lane l is key 8*(i/4) + 4*(l/32) + i%4
   // of row l%32, which is exactly the B operand layout of k-steps 0 (i < 8) and 1
@@ -387,6 +356,12 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
                                                                c.lane * 16) = pk[0];
   *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + c.wave * 2048 + 1024 +
                                                                c.lane * 16) = pk[1];
+  if (PRECISE) {
+    *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + PBUF_LO + c.wave * 2048 +
+                                                                 c.lane * 16) = pl[0];
+    *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+        pbuf + PBUF_LO + c.wave * 2048 + 1024 + c.lane * 16) = pl[1];
+  }
   __syncthreads();  // P^T of all 128 rows is in pbuf
   // O^T[dims of db, rows of rb] += V^T . P^T; k-step kst covers keys
   // 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.  A operand (dim block db of
@@ -405,23 +380,46 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
   auto pv_b = [&](int kst, int rb) -> bf16x8 {
     return *reinterpret_cast<lds_bf16x8*>(pb + rb * 2048 + kst * 1024);
   };
-  // all 8 B operands stay live; the A operands of one dim block (both k-steps)
-  // are read while the previous block's 8 MFMAs run
-  bf16x8 B[2][4], A[2][2];
+  if (!PRECISE) {
+    // all 8 B operands stay live; the A operands of one dim block (both
+    // k-steps) are read while the previous block's 8 MFMAs run
+    bf16x8 B[2][4], A[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) B[0][i] = pv_b(0, i);
-  A[0][0] = pv_a(0, 0);
+    for (int i = 0; i < 4; ++i) B[0][i] = pv_b(0, i);
+    A[0][0] = pv_a(0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) B[1][i] = pv_b(1, i);
-  A[0][1] = pv_a(1, 0);
+    for (int i = 0; i < 4; ++i) B[1][i] = pv_b(1, i);
+    A[0][1] = pv_a(1, 0);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int cur = db & 1;
+    for (int db = 0; db < 4; ++db) {
+      const int cur = db & 1;
+#pragma unroll
+      for (int kst = 0; kst < 2; ++kst) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[cur][kst], B[kst][rb]);
+        if (db + 1 < 4) A[cur ^ 1][kst] = pv_a(kst, db + 1);
+      }
+    }
+  } else {
+    // k-step outer: the 4 hi and 4 lo B operands of one k-step stay live, each
+    // A operand feeds 8 MFMAs
 #pragma unroll
     for (int kst = 0; kst < 2; ++kst) {
+      bf16x8 Bh[4], Bl[4], A[2];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[cur][kst], B[kst][rb]);
-      if (db + 1 < 4) A[cur ^ 1][kst] = pv_a(kst, db + 1);
+      for (int i = 0; i < 4; ++i) {
+        Bh[i] = pv_b(kst, i);
+        Bl[i] = *reinterpret_cast<lds_bf16x8*>(pb + PBUF_LO + i * 2048 + kst * 1024);
+      }
+      A[0] = pv_a(kst, 0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        if (db + 1 < 4) A[(db + 1) & 1] = pv_a(kst, db + 1);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[db & 1], Bh[rb]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[db & 1], Bl[rb]);
+      }
     }
   }
   // slots of tile t+3, for the gather issued by the next tile's body; loaded
@@ -435,7 +433,7 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
 // executed cold once per workgroup, so it is kept to one copy.  Returns true
 // if a restart is needed; every wave reads the flag after the same final
 // barrier.
-template <bool WIDE>
+template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ bool run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
                                           lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
                                           f32x16 (&O)[16], float& m_ref, float& m_true,
@@ -453,7 +451,7 @@ __device__ __forceinline__ bool run_split(lds_u8* stages, const SplitCtx& c, con
   for (int t = 0; t < nt; ++t) {
     tile_head(c, t, nt);
     const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;
-    tile_body<WIDE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, slot, c, qrope, pbuf, qf,
+    tile_body<WIDE, PRECISE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, slot, c, qrope, pbuf, qf,
                     O, m_ref, m_true, l_sum, flag);
     cur = cur == NSTAGE - 1 ? 0 : cur + 1;
   }
@@ -473,7 +471,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
 }
 
-template <int OUT, bool WIDE>
+template <int OUT, bool WIDE, bool PRECISE>
 __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
@@ -482,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     float* __restrict__ ws_lse_, SplitScalars p) {
   __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t qrope_s[ROWS_PER_WG * QR_ROW];
-  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[4 * 2 * 64 * 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[PRECISE ? 2 * PBUF_LO : PBUF_LO];
   __shared__ float inv_s[ROWS_PER_WG];
   __shared__ int restart_flag;
   lds_u8* const stages = (lds_u8*)stages_s;
@@ -597,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
       m_ref = m_pre;
       l_sum = 0.f;
       if (pass > 0) zero_acc(O);
-      if (!run_split<WIDE>(stages, c, qrope, pbuf, qf, O, m_ref, m_true, l_sum, &restart_flag))
+      if (!run_split<WIDE, PRECISE>(stages, c, qrope, pbuf, qf, O, m_ref, m_true, l_sum, &restart_flag))
         break;
       // a score exceeded its reference by more than 2^TAU: redo the split with
       // every row's reference at its true maximum (no score can exceed it)
@@ -673,91 +671,8 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   }
 }
 
-// ---------------------------------------------------------------- merge kernel
-
-// One row per workgroup.  Thread t owns value dims 4*(t & 127) .. +3; the two
-// halves of the workgroup take alternate splits (8 loads in flight per thread)
-// and combine through LDS.
-template <int OUT>
-__global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
-  constexpr int U = 8;
-  __shared__ f32x4 part_o[128];
-  __shared__ float part_w[128];
-  const int b = blockIdx.y;
-  const int q0 = p.qo_indptr[b];
-  const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
-  const int r = blockIdx.x;
-  if (r >= R) return;
-  const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
-  const int ns = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
-  if (ns <= 1) return;  // written directly by the split kernel
-  const int64_t g = (int64_t)q0 * p.num_heads + r;
-  const float* ls = p.ws_lse + g * p.max_splits;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += U) {
-    float v[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) v[j] = s0 + j < ns ? ls[s0 + j] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < U; ++j) M = fmaxf(M, v[j]);
-  }
-  const int t = threadIdx.x;
-  const int d = (t & 127) * 4;
-  const int h = t >> 7;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float W = 0.f;
-  if (M != -INFINITY) {
-    const float* po = p.ws_o + g * p.max_splits * VD + d;
-    for (int s0 = h; s0 < ns; s0 += 2 * U) {
-      float wgt[U];
-      f32x4 v[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int s = s0 + 2 * j;
-        // exp(-inf) = 0 for an empty split, whose partial output is not read
-        wgt[j] = s < ns ? expf(ls[s] - M) : 0.f;
-        v[j] = wgt[j] > 0.f ? *reinterpret_cast<const f32x4*>(po + (int64_t)s * VD)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        acc += wgt[j] * v[j];
-        W += wgt[j];
-      }
-    }
-  }
-  if (h == 1) {
-    part_o[t & 127] = acc;
-    part_w[t & 127] = W;
-  }
-  __syncthreads();
-  if (h == 1) return;
-  acc += part_o[t];
-  W += part_w[t];
-  if (M != -INFINITY) acc *= 1.f / W;
-  const float lse = (M == -INFINITY) ? -INFINITY : M + logf(W);
-  if (t == 0) p.lse[g] = lse;
-  if (OUT == OUT_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + g * VD + d) = acc;
-  } else {
-    bf16x4 w;
-    w[0] = (__bf16)acc[0];
-    w[1] = (__bf16)acc[1];
-    w[2] = (__bf16)acc[2];
-    w[3] = (__bf16)acc[3];
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + g * VD + d) = w;
-  }
-}
-
 // Launches go through hipLaunchKernel, which reports this launch's own status
 // (a non-gfx950 device fails here: the library carries gfx950 code only).
-
-hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st) {
-  PackParams a = p;
-  void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&tv_pack_mask_kernel), dim3(grid_x, batch),
-                         dim3(256), args, 0, st);
-}
 
 hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st) {
   const uint16_t* q = p.q;
@@ -772,22 +687,17 @@ hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st)
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
   void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mw, &o, &l, &wo, &wl, &sc};
-  const void* fn;
-  if (p.wide)
-    fn = out == OUT_F32 ? reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true>)
-                        : reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, true>);
-  else
-    fn = out == OUT_F32 ? reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, false>)
-                        : reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false>);
+  // [out dtype][wide][precise]
+  static const void* const fns[2][2][2] = {
+      {{reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false, true>)},
+       {reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, true, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, true, true>)}},
+      {{reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, false, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, false, true>)},
+       {reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, true>)}}};
+  const void* fn = fns[out == OUT_F32][p.wide][p.precise];
   return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }
-
-hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, hipStream_t st) {
-  MergeParams a = p;
-  void* args[] = {&a};
-  const void* fn = out == OUT_F32 ? reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32>)
-                                  : reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16>);
-  return hipLaunchKernel(fn, dim3(grid_x, batch), dim3(256), args, 0, st);
-}
-
 }  // namespace tv
