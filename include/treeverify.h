@@ -58,10 +58,10 @@ typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
 
 /* tv_problem.flags.  The softmax probabilities (fp32) enter the P.V product on
  * the bf16 matrix cores.  By default each is rounded once to bf16, which bounds
- * the output error by 2^-9 * max |v| over the row's visible keys.
+ * the output error by 2^-8 * max |v| over the row's visible keys.
  * TV_FLAG_PRECISE_P splits each probability into two bf16 terms (hi + lo, about
  * 16 significant bits) and runs the P.V product on both: the error bound
- * becomes about 2^-17 * max |v| for 32 more MFMAs per 32-key tile (68 -> 100).
+ * becomes 2^-16 * max |v| for 32 more MFMAs per 32-key tile (68 -> 100).
  * Meant for value distributions with large outliers. */
 #define TV_FLAG_PRECISE_P 1
 

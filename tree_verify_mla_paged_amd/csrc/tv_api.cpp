@@ -57,6 +57,8 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   if (p->out_dtype != TV_OUT_BF16 && p->out_dtype != TV_OUT_F32) return TV_ERR_UNSUPPORTED;
   if ((p->flags & ~TV_FLAG_PRECISE_P) != 0 || p->reserved != 0) return TV_ERR_UNSUPPORTED;
   if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
+  // per-request key offsets are 32-bit byte offsets (4 * key) in the kernels
+  if (p->max_kv_len >= (1 << 30)) return TV_ERR_SHAPE;
   if ((int64_t)p->max_q_len * p->num_heads > kMaxInt32 ||
       p->total_q * (int64_t)p->num_heads > kMaxInt32)
     return TV_ERR_SHAPE;

@@ -37,14 +37,15 @@
 //    ds_read_b64_tr_b16 (within 16 lanes, output lane i element j comes from
 //    source lane 4j + i/4, element i%4: when source lane 4j+q points at dims
 //    d0+4q.. of key j, lane i gets keys j=0..3 at dim d0+i).
-//  * Reference maximum without rescaling: a row's reference is fixed at the
-//    maximum of its first tile with a visible key (O and l are still exactly 0
-//    then).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32 sums and
-//    bf16 operands hold exactly in range, so O is never rescaled in the loop and
-//    no VALU work ever touches the accumulators.  If some row's score exceeds
-//    its reference by more than TAU, the workgroup runs the split again with
-//    each row's reference preset to its true maximum over the split (tracked
-//    during the first pass), after which probabilities are <= 1.
+//  * Reference maximum with thresholded rescaling: a row's reference is set at
+//    the maximum of its first tile with a visible key (O and l are still
+//    exactly 0 then) and moves only when a score exceeds it by more than TAU
+//    (log2 units).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32
+//    sums and bf16 operands hold, so in the common case no VALU work touches
+//    the accumulators.  When a row's reference moves, its l and O are scaled by
+//    2^(old - new); the factor goes through LDS because every wave holds a
+//    slice of every row's O, and the whole workgroup takes that branch after
+//    the barrier that publishes P.
 //  * The kernel's straight-line code runs cold once per workgroup (instruction
 //    fetch), so prologue, loop and epilogue are kept compact: accumulators are
 //    zeroed by MFMAs, the epilogue is a rolled loop over LDS-staged rows.
@@ -64,6 +65,7 @@ constexpr int MASKW_BYTES = 4 * 64 * 4;   // 256 visibility words (one per draft
 constexpr int STAGE = MAIN_BYTES + ROPE_BYTES + MASKW_BYTES;  // 46080
 constexpr int NSTAGE = 3;
 constexpr int DMA_PER_TILE = 10;          // direct-to-LDS loads per wave per tile
+constexpr int SLOT_RING = 4;              // tiles of gather slots held per wave in LDS
 constexpr float TAU = 64.0f;              // log2 headroom of a probability over its reference
 
 // A key's 1024 latent bytes sit at key*ROW + key_shift(key).  Modulo 256 bytes
@@ -100,6 +102,7 @@ struct SplitCtx {
   int rp_off[4];
   bool row_ok;
   float scale_log2;
+  lds_u8* sring;            // this wave's ring of gather slots: SLOT_RING entries of 256 bytes
 };
 
 // Direct-to-LDS gathers, as inline asm: the compiler treats the equivalent
@@ -131,23 +134,36 @@ __device__ __forceinline__ int fresh(int v) {
   return v;
 }
 
-// Slots of this wave's 8 keys (8*wave .. 8*wave+7) of tile t: wave-uniform
-// scalar loads, clamped to the split's last key.  Tiles past the split (the
-// loop runs a multiple of 3 tiles) therefore gather real, finite rows, and their
-// keys are masked off, so they contribute exactly 0.
-__device__ __forceinline__ void load_slots(int (&slot)[8], const SplitCtx& c, int t) {
-  const int kt = c.kbeg + t * TILE + 8 * c.wave;
-  const int last = c.kend - 1;
-  // written out: every index of slot[] must be a constant before loop
-  // unrolling, or the array is moved to memory
-  slot[0] = c.idx[min(kt + 0, last)];
-  slot[1] = c.idx[min(kt + 1, last)];
-  slot[2] = c.idx[min(kt + 2, last)];
-  slot[3] = c.idx[min(kt + 3, last)];
-  slot[4] = c.idx[min(kt + 4, last)];
-  slot[5] = c.idx[min(kt + 5, last)];
-  slot[6] = c.idx[min(kt + 6, last)];
-  slot[7] = c.idx[min(kt + 7, last)];
+// Slots of this wave's 8 keys of tile t, gathered into ring entry t % SLOT_RING
+// by one direct-to-LDS dword load (lane l: key 8*wave + (l & 7)), clamped to
+// the split's last key: keys past the split gather real, finite rows, which are
+// masked off and contribute exactly 0.  In the loop it is issued four tiles
+// ahead, before the gathers of an earlier tile, so the vmcnt wait that makes
+// that tile readable also covers it, and the slots are then plain LDS reads: no
+// scalar load is ever pending in the tile loop (a pending one would turn every
+// LDS wait into a full wait).
+__device__ __forceinline__ void slot_dma(const SplitCtx& c, int t) {
+  const int k = min(c.kbeg + t * TILE + 8 * c.wave + (fresh(c.lane) & 7), c.kend - 1);
+  dma4_s((uint32_t)k * 4u, c.idx, lds_addr(c.sring) + 256 * (t % SLOT_RING));
+}
+
+// The 8 slots as wave-uniform values, and the slot of key 8*wave + lane/8 (the
+// RoPE gather's) per lane.
+__device__ __forceinline__ void read_slots(int (&slot)[8], int& slane, const SplitCtx& c, int t) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const lds_u8* e = c.sring + 256 * (t % SLOT_RING);
+  slane = *reinterpret_cast<const __attribute__((address_space(3))) int*>(
+      e + 4 * (fresh(c.lane) >> 3));
+  const i32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e);
+  const i32x4 b = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e + 16);
+  slot[0] = __builtin_amdgcn_readfirstlane(a[0]);
+  slot[1] = __builtin_amdgcn_readfirstlane(a[1]);
+  slot[2] = __builtin_amdgcn_readfirstlane(a[2]);
+  slot[3] = __builtin_amdgcn_readfirstlane(a[3]);
+  slot[4] = __builtin_amdgcn_readfirstlane(b[0]);
+  slot[5] = __builtin_amdgcn_readfirstlane(b[1]);
+  slot[6] = __builtin_amdgcn_readfirstlane(b[2]);
+  slot[7] = __builtin_amdgcn_readfirstlane(b[3]);
 }
 
 __device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint32_t m0) {
@@ -167,7 +183,7 @@ __device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint3
 // taken by reference to the caller's array (a pointer kept in a struct makes
 // the compiler move the array to memory).
 template <bool WIDE, int J>
-__device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)[8],
+__device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)[8], int slane,
                                              const SplitCtx& c, int t) {
   if constexpr (J < 8) {
     const uint32_t m0 = lds_addr(sb) + 8 * c.wave * ROW + 32 * (c.wave & 1) + J * ROW +
@@ -177,18 +193,9 @@ __device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)
     // recomputed every tile from an opaque copy of the lane id: a hoisted,
     // loop-invariant per-lane offset would be spilled, and its reload (a
     // vector memory op) would wait out the gathers just issued
-    int lane = c.lane;
-    asm volatile("" : "+v"(lane));
-    const int k = lane >> 3;  // key 8*wave + k, RoPE chunk slot lane & 7
-    // the per-lane choice among the 8 slots is made on opaque values: a select
-    // between loads of slot[] would be folded into a per-lane indexed load,
-    // which moves the whole array to memory
-    int s0 = slot[0], s1 = slot[1], s2 = slot[2], s3 = slot[3];
-    int s4 = slot[4], s5 = slot[5], s6 = slot[6], s7 = slot[7];
-    asm volatile("" : "+s"(s0), "+s"(s1), "+s"(s2), "+s"(s3), "+s"(s4), "+s"(s5), "+s"(s6),
-                 "+s"(s7));
-    const int s = k < 4 ? (k < 2 ? (k == 0 ? s0 : s1) : (k == 2 ? s2 : s3))
-                        : (k < 6 ? (k == 4 ? s4 : s5) : (k == 6 ? s6 : s7));
+    const int lane = fresh(c.lane);
+    const int k = lane >> 3;  // key 8*wave + k (slot slane), RoPE chunk slot lane & 7
+    const int s = slane;
     const int pos = 8 * c.wave + k;
     const uint32_t chunk = (uint32_t)((lane & 7) ^ rope_swz(pos));
     const uint32_t m0 = lds_addr(sb) + MAIN_BYTES + 8 * c.wave * 128;
@@ -204,19 +211,19 @@ __device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)
 }
 
 template <bool WIDE>
-__device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], const SplitCtx& c,
-                                           int t) {
+__device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], int slane,
+                                           const SplitCtx& c, int t) {
   static_assert(DMA_PER_TILE == 10, "");
-  gather_piece<WIDE, 0>(sb, slot, c, t);
-  gather_piece<WIDE, 1>(sb, slot, c, t);
-  gather_piece<WIDE, 2>(sb, slot, c, t);
-  gather_piece<WIDE, 3>(sb, slot, c, t);
-  gather_piece<WIDE, 4>(sb, slot, c, t);
-  gather_piece<WIDE, 5>(sb, slot, c, t);
-  gather_piece<WIDE, 6>(sb, slot, c, t);
-  gather_piece<WIDE, 7>(sb, slot, c, t);
-  gather_piece<WIDE, 8>(sb, slot, c, t);
-  gather_piece<WIDE, 9>(sb, slot, c, t);
+  gather_piece<WIDE, 0>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 1>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 2>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 3>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 4>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 5>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 6>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 7>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 8>(sb, slot, slane, c, t);
+  gather_piece<WIDE, 9>(sb, slot, slane, c, t);
 }
 
 // The MFMAs of the tile loop are inline asm: S^T accumulates in VGPRs and O^T
@@ -306,20 +313,20 @@ __device__ __forceinline__ float scores(float (&x)[16], const f32x16& acc, uint3
   return fmaxf(tmax, __shfl_xor(tmax, 32));
 }
 
-// Pipeline head of tile t: once this wave's gathers of tile t have landed (at
-// most tile t+1's are outstanding) and every wave has passed the barrier, the
-// stage of tile t is readable and the stage of tile t-1 is free.
+// Pipeline head of tile t: once this wave's gathers of tile t have landed and
+// every wave has passed the barrier, the stage of tile t is readable and the
+// stage of tile t-1 is free.  Issued after tile t's gathers: the slot gather of
+// tile t+3 and, if it exists, tile t+1's gathers (loads complete in order).
 __device__ __forceinline__ void tile_head(const SplitCtx& c, int t, int nt) {
-  if (t + 1 < nt) wait_vmcnt<DMA_PER_TILE>();
-  else wait_vmcnt<0>();
+  if (t + 1 < nt) wait_vmcnt<DMA_PER_TILE + 1>();
+  else wait_vmcnt<1>();
   __syncthreads();
 }
 
 // Pipeline body of tile t (stage sb): gather tile t+2 into stage sg, then
-// consume tile t.  m_true tracks each row's maximum over all tiles; a score
-// above the row's reference by more than 2^TAU raises *flag (the pass is then
-// redone with the reference preset to m_true; this pass's accumulators,
-// possibly non-finite by then, are discarded).
+// consume tile t.  A score above its row's reference by more than TAU moves
+// the reference (see the file notes): rflag[t & 1] tells every wave, after the
+// P barrier, to scale its O rows by alpha_s before this tile's PV.
 //
 // QK and the softmax are row-partitioned (wave w: rows 32w..32w+31); PV is
 // dim-partitioned (wave w: value dims 128w..128w+127 of all 128 rows), so each
@@ -327,18 +334,31 @@ __device__ __forceinline__ void tile_head(const SplitCtx& c, int t, int nt) {
 // the two through pbuf: [row block][k-step][lane] 16-byte MFMA B operands.
 template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, int nt,
-                                          int (&slot)[8], const SplitCtx& c,
+                                          const SplitCtx& c,
                                           const lds_u8* qrope, lds_u8* pbuf,
                                           const bf16x8 (&qf)[VD / 16], f32x16 (&O)[16],
-                                          float& m_ref, float& m_true, float& l_sum, int* flag) {
-  if (t + 2 < nt) issue_tile<WIDE>(sg, slot, c, t + 2);
+                                          float& m_ref, float& l_sum, float* alpha_s, int* rflag) {
+  slot_dma(c, t + 4);
+  if (t + 2 < nt) {
+    int slot[8], slane;
+    read_slots(slot, slane, c, t + 2);
+    issue_tile<WIDE>(sg, slot, slane, c, t + 2);
+  }
   const uint32_t mw = tile_mask(sb, c, t);
   const f32x16 acc = qk_tile(sb, qrope, qf, c);
   float x[16];
   const float tmax = scores(x, acc, mw, c);
-  m_true = fmaxf(m_true, tmax);
   if (m_ref == -INFINITY) m_ref = tmax;  // first visible keys: O and l are still 0
-  if (__any(tmax > m_ref + TAU) && c.lane == 0) *flag = 1;
+  const bool jump = tmax > m_ref + TAU;
+  const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;
+  if (jump) {
+    l_sum *= alpha;
+    m_ref = tmax;
+  }
+  if (c.lane < 32) alpha_s[c.wave * 32 + c.lane] = alpha;
+  if (__any(jump) && c.lane == 0) rflag[t & 1] = 1;
+  // the other flag was last read in tile t-1, before this tile's first barrier
+  if (c.wave == 0 && c.lane == 0) rflag[(t + 1) & 1] = 0;
   const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
   bf16x8 pk[2], pl[2];
 #pragma unroll
@@ -362,7 +382,29 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
     *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
         pbuf + PBUF_LO + c.wave * 2048 + 1024 + c.lane * 16) = pl[1];
   }
-  __syncthreads();  // P^T of all 128 rows is in pbuf
+  __syncthreads();  // P^T of all 128 rows is in pbuf, rflag and alpha_s are set
+  if (__builtin_amdgcn_readfirstlane(rflag[t & 1])) {
+    // some row's reference moved: scale this wave's O slice of every row
+    // (accumulator O[4*db + rb] holds rows 32*rb + lane % 32)
+    float a4[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) a4[rb] = alpha_s[32 * rb + (c.lane & 31)];
+    // element by element, in place in the AGPRs: O must never have a
+    // definition outside the accumulator register class in the loop
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float tmp;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(O[i][r]), "=&v"(tmp)
+            : "v"(a4[i & 3]));
+      }
+    }
+  }
   // O^T[dims of db, rows of rb] += V^T . P^T; k-step kst covers keys
   // 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.  A operand (dim block db of
   // this wave) = two transposed 8-byte reads; B operand (row block rb) = pbuf.
@@ -422,43 +464,48 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
       }
     }
   }
-  // slots of tile t+3, for the gather issued by the next tile's body; loaded
-  // last so no scalar load is outstanding while the LDS reads above pipeline
-  if (t + 3 < nt) load_slots(slot, c, t + 3);
 }
 
-// All tiles of the split (c.ntiles >= 1), one loop body: the stage of tile t
-// is chosen at run time (the gathers are inline asm, invisible to the
-// compiler's alias analysis, so a run-time stage costs no waits).  The code is
-// executed cold once per workgroup, so it is kept to one copy.  Returns true
-// if a restart is needed; every wave reads the flag after the same final
-// barrier.
-template <bool WIDE, bool PRECISE>
-__device__ __forceinline__ bool run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
-                                          lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
-                                          f32x16 (&O)[16], float& m_ref, float& m_true,
-                                          float& l_sum, int* flag) {
-  const int nt = c.ntiles;
-  int slot[8];
-  load_slots(slot, c, 0);
-  issue_tile<WIDE>(stages, slot, c, 0);
-  if (nt > 1) {
-    load_slots(slot, c, 1);
-    issue_tile<WIDE>(stages + STAGE, slot, c, 1);
+// Start of a pass over the split (c.ntiles >= 1; nothing else outstanding):
+// the slots of tiles 0 and 1 (waited for here), then the slot gathers of tiles
+// 2 and 3 and the gathers of tiles 0 and 1, in the order tile_head accounts for.
+template <bool WIDE>
+__device__ __forceinline__ void split_start(lds_u8* stages, const SplitCtx& c) {
+  int slot[8], slane;
+  slot_dma(c, 0);
+  slot_dma(c, 1);
+  wait_vmcnt<0>();
+  read_slots(slot, slane, c, 0);
+  slot_dma(c, 2);
+  issue_tile<WIDE>(stages, slot, slane, c, 0);
+  slot_dma(c, 3);
+  if (c.ntiles > 1) {
+    read_slots(slot, slane, c, 1);
+    issue_tile<WIDE>(stages + STAGE, slot, slane, c, 1);
   }
-  if (nt > 2) load_slots(slot, c, 2);
+}
+
+// All tiles of the split (c.ntiles >= 1) after split_start, one loop body: the
+// stage of tile t is chosen at run time (the gathers are inline asm, invisible
+// to the compiler's alias analysis, so a run-time stage costs no waits).  The
+// code is executed cold once per workgroup, so it is kept to one copy.
+template <bool WIDE, bool PRECISE>
+__device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
+                                          lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
+                                          f32x16 (&O)[16], float& m_ref, float& l_sum,
+                                          float* alpha_s, int* rflag) {
+  const int nt = c.ntiles;
   int cur = 0;  // stage of tile t; tile t+2 goes to the stage of tile t-1
   for (int t = 0; t < nt; ++t) {
     tile_head(c, t, nt);
     const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;
-    tile_body<WIDE, PRECISE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, slot, c, qrope, pbuf, qf,
-                    O, m_ref, m_true, l_sum, flag);
+    tile_body<WIDE, PRECISE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, c, qrope, pbuf, qf,
+                    O, m_ref, l_sum, alpha_s, rflag);
     cur = cur == NSTAGE - 1 ? 0 : cur + 1;
   }
-  // drain: no gather may still be writing a stage when another pass reuses it
+  // drain: no gather may still be writing LDS when the epilogue reuses it
   wait_vmcnt<0>();
   __syncthreads();
-  return *flag != 0;
 }
 
 // O = 0 by MFMAs with zero operands: 16 instructions instead of 256
@@ -482,7 +529,9 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t qrope_s[ROWS_PER_WG * QR_ROW];
   __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[PRECISE ? 2 * PBUF_LO : PBUF_LO];
   __shared__ float inv_s[ROWS_PER_WG];
-  __shared__ int restart_flag;
+  __shared__ __attribute__((aligned(1024))) uint8_t sring_s[4 * SLOT_RING * 256];
+  __shared__ float alpha_s[ROWS_PER_WG];
+  __shared__ int rflag_s[2];
   lds_u8* const stages = (lds_u8*)stages_s;
   lds_u8* const qrope = (lds_u8*)qrope_s;
   lds_u8* const pbuf = (lds_u8*)pbuf_s;
@@ -522,6 +571,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   c.wave = wave;
   c.lane = lane;
   c.scale_log2 = p.scale_log2;
+  c.sring = (lds_u8*)sring_s + wave * (SLOT_RING * 256);
 
   const int i0 = row0 / H;
   const int nd = (min(row0 + ROWS_PER_WG, R) - 1) / H - i0 + 1;
@@ -552,6 +602,10 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   }
   c.mw_off = MAIN_BYTES + ROPE_BYTES + 4 * dl;
 
+  // the first two tiles' gathers go out before the query rows are loaded, so
+  // their memory latency overlaps the loads below
+  if (c.ntiles > 0) split_start<WIDE>(stages, c);
+
   // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7): the 512
   // latent dims into VGPRs, the 64 RoPE dims of all 128 rows into LDS.  A row
   // past the request's rows uses the block's first row instead: its scores stay
@@ -578,6 +632,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   // steady state waits out the tile gathers instead
 #pragma unroll
   for (int ks = 0; ks < VD / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
+  if (tid < 2) rflag_s[tid] = 0;
   __syncthreads();
 
   // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
@@ -586,24 +641,8 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   zero_acc(O);
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
-  if (c.ntiles > 0) {
-    if (tid == 0) restart_flag = 0;
-    __syncthreads();
-    float m_pre = -INFINITY;
-    for (int pass = 0; pass < 2; ++pass) {
-      float m_true = -INFINITY;
-      m_ref = m_pre;
-      l_sum = 0.f;
-      if (pass > 0) zero_acc(O);
-      if (!run_split<WIDE, PRECISE>(stages, c, qrope, pbuf, qf, O, m_ref, m_true, l_sum, &restart_flag))
-        break;
-      // a score exceeded its reference by more than 2^TAU: redo the split with
-      // every row's reference at its true maximum (no score can exceed it)
-      m_pre = m_true;
-      if (tid == 0) restart_flag = 0;
-      __syncthreads();
-    }
-  }
+  if (c.ntiles > 0)
+    run_split<WIDE, PRECISE>(stages, c, qrope, pbuf, qf, O, m_ref, l_sum, alpha_s, rflag_s);
 
   // the last PV MFMAs must finish before O is read out of the AGPRs
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
