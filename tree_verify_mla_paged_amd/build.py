@@ -12,6 +12,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # packed fp32 VALU ops stay off (see the kernel notes)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the split kernel's software-pipelined QK chain (36 MFMAs with other
+         # work between them) must unroll fully; it exceeds the default limit
+         "-mllvm", "-pragma-unroll-threshold=1000000",
          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
 
 

@@ -139,7 +139,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     pp.qo_indptr = qo_indptr;
     pp.words = words;
     pp.max_tiles = lay.max_tiles;
-    const int64_t gx = ceil_div((int64_t)p->max_q_len * lay.max_tiles, 8);
+    const int64_t gx = ceil_div((int64_t)p->max_q_len * lay.max_tiles, 256);  // a word per thread
     if (gx > kMaxInt32) return TV_ERR_SHAPE;
     if (tv::launch_pack(pp, (int)gx, p->batch, s) != hipSuccess) return TV_ERR_LAUNCH;
   }

@@ -13,30 +13,29 @@
 
 namespace tv {
 
-// Word (token qo_indptr[b] + i, tile) bit k = mask byte of key 32*tile + k of draft i.
-// Each half-wave (32 lanes) builds one word; keys at or past L_b give 0.
+// Word (token qo_indptr[b] + i, tile) bit k = mask byte of key 32*tile + k of draft i;
+// keys at or past L_b give 0.  One word per thread: consecutive threads take
+// consecutive tiles of a draft row, so a wave reads 64 consecutive 32-byte
+// runs, all 32 byte loads of a thread in flight at once.
 __global__ __launch_bounds__(256) void tv_pack_mask_kernel(PackParams p) {
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
   const int n = p.qo_indptr[b + 1] - q0;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
   const int tiles = (L + TILE_KEYS - 1) / TILE_KEYS;
-  const int words = n * tiles;
-  const int w = blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int k = threadIdx.x & 31;
-  bool vis = false;
-  int i = 0, tile = 0;
-  if (w < words) {
-    i = w / tiles;
-    tile = w - i * tiles;
-    const int key = tile * TILE_KEYS + k;
-    if (key < L) vis = p.mask[p.mask_indptr[b] + (int64_t)i * L + key] != 0;
-  }
-  const uint64_t bits = __ballot(vis);
-  if (w < words && k == 0) {
-    const uint32_t word = (threadIdx.x & 32) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
-    p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = word;
-  }
+  const int w = blockIdx.x * 256 + threadIdx.x;
+  if (w >= n * tiles) return;
+  const int i = w / tiles;
+  const int tile = w - i * tiles;
+  const int nk = min(TILE_KEYS, L - tile * TILE_KEYS);
+  const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * L + tile * TILE_KEYS;
+  uint8_t v[TILE_KEYS];
+#pragma unroll
+  for (int k = 0; k < TILE_KEYS; ++k) v[k] = k < nk ? m[k] : 0;
+  uint32_t word = 0;
+#pragma unroll
+  for (int k = 0; k < TILE_KEYS; ++k) word |= (v[k] != 0 ? 1u : 0u) << k;
+  p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = word;
 }
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st) {

@@ -230,17 +230,21 @@ __device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], int
 // in the 256 AGPRs, which the compiler's own allocation does not achieve (it
 // puts both in AGPRs and evicts an O block), and `volatile` keeps the LDS
 // operand reads issued ahead of them where the source puts them.  Hazards the
-// compiler cannot see are covered here: every MFMA starts with s_nop 1 (a
-// VALU write of an operand register right before it); results are waited out
-// (mfma_drain) before anything but another MFMA reads them.
+// compiler cannot see are covered here: in the tile loop every MFMA operand
+// comes from an LDS read or the loop-invariant query registers (never from a
+// VALU write just before), the two places where VALU writes feed MFMAs
+// (zero_acc, the O rescale) end with s_nop, and results are waited out
+// (mfma_drain) before anything but another MFMA reads them.  (One issue slot
+// per instruction is what a single wave per SIMD gets: the loop avoids any
+// instruction it does not need.)
 __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_first_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_acc_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // >= 19 wait states: a 16-pass MFMA result may be read by VALU / v_accvgpr_read
 __device__ __forceinline__ void mfma_drain_v(f32x16& acc) {
@@ -313,76 +317,148 @@ __device__ __forceinline__ float scores(float (&x)[16], const f32x16& acc, uint3
   return fmaxf(tmax, __shfl_xor(tmax, 32));
 }
 
-// Pipeline head of tile t: once this wave's gathers of tile t have landed and
-// every wave has passed the barrier, the stage of tile t is readable and the
-// stage of tile t-1 is free.  Issued after tile t's gathers: the slot gather of
-// tile t+3 and, if it exists, tile t+1's gathers (loads complete in order).
-__device__ __forceinline__ void tile_head(const SplitCtx& c, int t, int nt) {
-  if (t + 1 < nt) wait_vmcnt<DMA_PER_TILE + 1>();
-  else wait_vmcnt<1>();
-  __syncthreads();
+// Register fence: as far as the compiler knows `v` is redefined here, so work
+// reading it stays below this point and work producing it stays above.  The
+// software pipeline below places its steps between chosen MFMAs this way.
+template <typename T>
+__device__ __forceinline__ void fence(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
-// Pipeline body of tile t (stage sb): gather tile t+2 into stage sg, then
-// consume tile t.  A score above its row's reference by more than TAU moves
-// the reference (see the file notes): rflag[t & 1] tells every wave, after the
-// P barrier, to scale its O rows by alpha_s before this tile's PV.
-//
-// QK and the softmax are row-partitioned (wave w: rows 32w..32w+31); PV is
-// dim-partitioned (wave w: value dims 128w..128w+127 of all 128 rows), so each
-// wave reads a quarter of the V tile instead of all of it.  P^T moves between
-// the two through pbuf: [row block][k-step][lane] 16-byte MFMA B operands.
-template <bool WIDE, bool PRECISE>
-__device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, int nt,
-                                          const SplitCtx& c,
-                                          const lds_u8* qrope, lds_u8* pbuf,
-                                          const bf16x8 (&qf)[VD / 16], f32x16 (&O)[16],
-                                          float& m_ref, float& l_sum, float* alpha_s, int* rflag) {
-  slot_dma(c, t + 4);
-  if (t + 2 < nt) {
-    int slot[8], slane;
-    read_slots(slot, slane, c, t + 2);
-    issue_tile<WIDE>(sg, slot, slane, c, t + 2);
-  }
-  const uint32_t mw = tile_mask(sb, c, t);
-  const f32x16 acc = qk_tile(sb, qrope, qf, c);
-  float x[16];
-  const float tmax = scores(x, acc, mw, c);
-  if (m_ref == -INFINITY) m_ref = tmax;  // first visible keys: O and l are still 0
-  const bool jump = tmax > m_ref + TAU;
-  const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;
-  if (jump) {
-    l_sum *= alpha;
-    m_ref = tmax;
-  }
-  if (c.lane < 32) alpha_s[c.wave * 32 + c.lane] = alpha;
-  if (__any(jump) && c.lane == 0) rflag[t & 1] = 1;
-  // the other flag was last read in tile t-1, before this tile's first barrier
-  if (c.wave == 0 && c.lane == 0) rflag[(t + 1) & 1] = 0;
-  const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-  bf16x8 pk[2], pl[2];
+// QK chain of one tile (as qk_tile) calling bg(ks) after the MFMA of each
+// k-step: work that does not depend on the chain, issued in its shadow (with
+// one wave per SIMD every instruction takes an issue slot; an MFMA keeps the
+// matrix pipe busy for about eight of them).
+template <typename Bg>
+__device__ __forceinline__ f32x16 qk_tile_bg(const lds_u8* sb, const lds_u8* qrope,
+                                             const bf16x8 (&qf)[VD / 16], const SplitCtx& c,
+                                             Bg&& bg) {
+  constexpr int NK = QK / 16;
+  const lds_u8* qa = sb + c.qk_off;
+  const lds_u8* qr = qrope + fresh(c.qr_off);
+  auto a_addr = [&](int ks) -> const lds_u8* {
+    return ks < VD / 16 ? qa + 32 * ks : sb + c.rp_off[ks - VD / 16];
+  };
+  bf16x8 buf[QK_AHEAD], bq[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float e = __builtin_amdgcn_exp2f(x[i] - mu);
-    l_sum += e;
-    pk[i >> 3][i & 7] = (__bf16)e;
-    // PRECISE: the rounding residual, itself rounded to bf16 (hi + lo carries
-    // about 16 significant bits of e)
-    if (PRECISE) pl[i >> 3][i & 7] = (__bf16)(e - (float)pk[i >> 3][i & 7]);
+  for (int k = 0; k < QK_AHEAD; ++k) buf[k] = *reinterpret_cast<lds_bf16x8*>(a_addr(k));
+  f32x16 acc;
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    const bf16x8 a = buf[ks % QK_AHEAD];
+    const int nk = ks + QK_AHEAD;
+    if (nk < NK) {
+      buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(nk));
+      if (nk >= VD / 16)
+        bq[nk - VD / 16] = *reinterpret_cast<lds_bf16x8*>(qr + 32 * (nk - VD / 16));
+    }
+    const bf16x8 b = ks < VD / 16 ? qf[ks] : bq[ks - VD / 16];
+    if (ks == 0) mfma_first_v(acc, a, b);
+    else mfma_acc_v(acc, a, b);
+    bg(ks);
   }
-  // P^T of this wave's rows: register i of lane l is key 8*(i/4) + 4*(l/32) + i%4
-  // of row l%32, which is exactly the B operand layout of k-steps 0 (i < 8) and 1
-  *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + c.wave * 2048 +
-                                                               c.lane * 16) = pk[0];
-  *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + c.wave * 2048 + 1024 +
-                                                               c.lane * 16) = pk[1];
-  if (PRECISE) {
-    *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(pbuf + PBUF_LO + c.wave * 2048 +
-                                                                 c.lane * 16) = pl[0];
-    *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
-        pbuf + PBUF_LO + c.wave * 2048 + 1024 + c.lane * 16) = pl[1];
+  mfma_drain_v(acc);
+  return acc;
+}
+
+// The softmax of one tile, in steps small enough to sit between MFMAs.
+// S holds S^T of the wave's 32 rows (lane l: row l%32; register i: key
+// 8*(i/4) + 4*(l/32) + i%4), mw the row's visibility word of the tile.
+struct Soft {
+  float x[16];  // masked, scaled scores (log2 units), then probabilities
+  float tmax, mu;
+  bf16x8 pk[2], pl[2];
+};
+
+constexpr int SOFT_STEPS = 9;
+
+template <bool PRECISE>
+__device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, uint32_t mw,
+                                          const SplitCtx& c, lds_u8* pbuf, float& m_ref,
+                                          float& l_sum, float* alpha_s, int* rflag, int t) {
+  const uint32_t mh = mw >> (4 * (c.lane >> 5));  // see scores()
+  if (step == 0 || step == 1) {
+    fence(S);
+#pragma unroll
+    for (int i = 8 * step; i < 8 * step + 8; ++i) {
+      sm.x[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? S[i] * c.scale_log2 : -INFINITY;
+      fence(sm.x[i]);
+    }
+  } else if (step == 2) {
+    float m = sm.x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, sm.x[i]);
+    sm.tmax = fmaxf(m, __shfl_xor(m, 32));
+    fence(sm.tmax);
+  } else if (step == 3) {
+    // first visible keys set the reference (O and l are still 0); a score more
+    // than TAU above it moves it, and l and O are scaled by 2^(old - new)
+    if (m_ref == -INFINITY) m_ref = sm.tmax;
+    const bool jump = sm.tmax > m_ref + TAU;
+    const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - sm.tmax) : 1.f;
+    if (jump) {
+      l_sum *= alpha;
+      m_ref = sm.tmax;
+    }
+    if (c.lane < 32) alpha_s[c.wave * 32 + c.lane] = alpha;
+    if (__any(jump) && c.lane == 0) rflag[t & 1] = 1;
+    // the other flag was last read in tile t-1, before this tile's first barrier
+    if (c.wave == 0 && c.lane == 0) rflag[(t + 1) & 1] = 0;
+    sm.mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    fence(sm.mu);
+  } else if (step >= 4 && step < 8) {
+#pragma unroll
+    for (int i = 4 * (step - 4); i < 4 * (step - 4) + 4; ++i) {
+      const float e = __builtin_amdgcn_exp2f(sm.x[i] - sm.mu);
+      l_sum += e;
+      sm.pk[i >> 3][i & 7] = (__bf16)e;
+      // PRECISE: the rounding residual, itself rounded to bf16 (hi + lo
+      // carries about 16 significant bits of e)
+      if (PRECISE) sm.pl[i >> 3][i & 7] = (__bf16)(e - (float)sm.pk[i >> 3][i & 7]);
+    }
+    fence(l_sum);
+    fence(sm.pk[(step - 4) >> 1]);
+    if (PRECISE) fence(sm.pl[(step - 4) >> 1]);
+  } else if (step == 8) {
+    // P^T of this wave's rows: register i of lane l is key 8*(i/4) + 4*(l/32) +
+    // i%4 of row l%32, which is exactly the B operand layout of k-steps 0 (i < 8)
+    // and 1
+    typedef __attribute__((address_space(3))) bf16x8 lds_w16;
+    *reinterpret_cast<lds_w16*>(pbuf + c.wave * 2048 + c.lane * 16) = sm.pk[0];
+    *reinterpret_cast<lds_w16*>(pbuf + c.wave * 2048 + 1024 + c.lane * 16) = sm.pk[1];
+    if (PRECISE) {
+      *reinterpret_cast<lds_w16*>(pbuf + PBUF_LO + c.wave * 2048 + c.lane * 16) = sm.pl[0];
+      *reinterpret_cast<lds_w16*>(pbuf + PBUF_LO + c.wave * 2048 + 1024 + c.lane * 16) =
+          sm.pl[1];
+    }
   }
-  __syncthreads();  // P^T of all 128 rows is in pbuf, rflag and alpha_s are set
+}
+
+// gather_piece with the piece number known only after unrolling
+template <bool WIDE>
+__device__ __forceinline__ void gather_piece_n(int j, const lds_u8* sb, const int (&slot)[8],
+                                               int slane, const SplitCtx& c, int t) {
+  static_assert(DMA_PER_TILE == 10, "");
+  switch (j) {
+    case 0: gather_piece<WIDE, 0>(sb, slot, slane, c, t); break;
+    case 1: gather_piece<WIDE, 1>(sb, slot, slane, c, t); break;
+    case 2: gather_piece<WIDE, 2>(sb, slot, slane, c, t); break;
+    case 3: gather_piece<WIDE, 3>(sb, slot, slane, c, t); break;
+    case 4: gather_piece<WIDE, 4>(sb, slot, slane, c, t); break;
+    case 5: gather_piece<WIDE, 5>(sb, slot, slane, c, t); break;
+    case 6: gather_piece<WIDE, 6>(sb, slot, slane, c, t); break;
+    case 7: gather_piece<WIDE, 7>(sb, slot, slane, c, t); break;
+    case 8: gather_piece<WIDE, 8>(sb, slot, slane, c, t); break;
+    default: gather_piece<WIDE, 9>(sb, slot, slane, c, t); break;
+  }
+}
+
+// PV of tile t (stage sb), after the barrier that publishes P(t): first the O
+// rescale if some row's reference moved in this tile.
+template <bool PRECISE>
+__device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds_u8* pbuf,
+                                        f32x16 (&O)[16], const float* alpha_s, const int* rflag,
+                                        int t) {
   if (__builtin_amdgcn_readfirstlane(rflag[t & 1])) {
     // some row's reference moved: scale this wave's O slice of every row
     // (accumulator O[4*db + rb] holds rows 32*rb + lane % 32)
@@ -404,6 +480,7 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
             : "v"(a4[i & 3]));
       }
     }
+    asm volatile("s_nop 3");  // accumulator writes before the next MFMA reads them
   }
   // O^T[dims of db, rows of rb] += V^T . P^T; k-step kst covers keys
   // 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.  A operand (dim block db of
@@ -466,42 +543,78 @@ __device__ __forceinline__ void tile_body(const lds_u8* sb, lds_u8* sg, int t, i
   }
 }
 
-// Start of a pass over the split (c.ntiles >= 1; nothing else outstanding):
-// the slots of tiles 0 and 1 (waited for here), then the slot gathers of tiles
-// 2 and 3 and the gathers of tiles 0 and 1, in the order tile_head accounts for.
+// Start of the split (c.ntiles >= 1; nothing outstanding): the slots of tiles
+// 0 and 1 (waited for here) and 2, then the gathers of tiles 0 and 1.
 template <bool WIDE>
 __device__ __forceinline__ void split_start(lds_u8* stages, const SplitCtx& c) {
   int slot[8], slane;
   slot_dma(c, 0);
   slot_dma(c, 1);
+  slot_dma(c, 2);
   wait_vmcnt<0>();
   read_slots(slot, slane, c, 0);
-  slot_dma(c, 2);
   issue_tile<WIDE>(stages, slot, slane, c, 0);
-  slot_dma(c, 3);
   if (c.ntiles > 1) {
     read_slots(slot, slane, c, 1);
     issue_tile<WIDE>(stages + STAGE, slot, slane, c, 1);
   }
 }
 
-// All tiles of the split (c.ntiles >= 1) after split_start, one loop body: the
-// stage of tile t is chosen at run time (the gathers are inline asm, invisible
-// to the compiler's alias analysis, so a run-time stage costs no waits).  The
-// code is executed cold once per workgroup, so it is kept to one copy.
+// All tiles of the split after split_start, software-pipelined: iteration t
+// runs QK of tile t+1 with, in the shadow of its MFMAs, the gathers of tile t+2
+// (and the slots of t+3) and the softmax of tile t; then, after the barrier
+// that publishes P(t), the PV of tile t.  Tile k sits in stage k % 3: at
+// iteration t stage t (PV), t+1 (QK) and t+2 (being gathered).  Every gather
+// issued before iteration t's barrier has landed by then (vmcnt(0): the
+// iteration issues nothing else to global memory).
 template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
                                           lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
                                           f32x16 (&O)[16], float& m_ref, float& l_sum,
                                           float* alpha_s, int* rflag) {
   const int nt = c.ntiles;
-  int cur = 0;  // stage of tile t; tile t+2 goes to the stage of tile t-1
+  // tile 0: its gathers landed (only tile 1's may be outstanding), QK
+  if (nt > 1) wait_vmcnt<DMA_PER_TILE>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  uint32_t mw = tile_mask(stages, c, 0);
+  f32x16 S = qk_tile(stages, qrope, qf, c);
+  int cur = 0;  // stage of tile t
   for (int t = 0; t < nt; ++t) {
-    tile_head(c, t, nt);
-    const int nxt = cur == 0 ? NSTAGE - 1 : cur - 1;
-    tile_body<WIDE, PRECISE>(stages + cur * STAGE, stages + nxt * STAGE, t, nt, c, qrope, pbuf, qf,
-                    O, m_ref, l_sum, alpha_s, rflag);
-    cur = cur == NSTAGE - 1 ? 0 : cur + 1;
+    const int nx1 = cur == NSTAGE - 1 ? 0 : cur + 1;  // stage of tile t+1
+    const int nx2 = cur == 0 ? NSTAGE - 1 : cur - 1;  // stage of tile t+2
+    if (t + 1 < nt) wait_vmcnt<0>();
+    __syncthreads();  // tile t+1 readable; every wave is done with PV(t-1)
+    Soft sm;
+    uint32_t mw_next = 0;
+    int slot[8], slane = 0;
+    const bool gather = t + 2 < nt;
+    auto bg = [&](int ks) {
+      if (ks == 0) {
+        if (gather) read_slots(slot, slane, c, t + 2);
+        slot_dma(c, t + 3);
+      } else if (ks <= DMA_PER_TILE) {
+        if (gather) gather_piece_n<WIDE>(ks - 1, stages + nx2 * STAGE, slot, slane, c, t + 2);
+      } else if (ks == DMA_PER_TILE + 1) {
+        if (t + 1 < nt) mw_next = tile_mask(stages + nx1 * STAGE, c, t + 1);
+      } else if (ks >= 12 && ks < 12 + 2 * SOFT_STEPS && (ks & 1) == 0) {
+        soft_step<PRECISE>((ks - 12) >> 1, sm, S, mw, c, pbuf, m_ref, l_sum, alpha_s, rflag, t);
+      }
+    };
+    f32x16 S_next;
+    if (t + 1 < nt) {
+      S_next = qk_tile_bg(stages + nx1 * STAGE, qrope, qf, c, bg);
+    } else {
+      // last tile: nothing left to hide the softmax behind
+#pragma unroll
+      for (int st = 0; st < SOFT_STEPS; ++st)
+        soft_step<PRECISE>(st, sm, S, mw, c, pbuf, m_ref, l_sum, alpha_s, rflag, t);
+    }
+    __syncthreads();  // P(t) of all 128 rows is in pbuf, rflag and alpha_s are set
+    pv_tile<PRECISE>(stages + cur * STAGE, c, pbuf, O, alpha_s, rflag, t);
+    S = S_next;
+    mw = mw_next;
+    cur = nx1;
   }
   // drain: no gather may still be writing LDS when the epilogue reuses it
   wait_vmcnt<0>();
@@ -512,7 +625,7 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, con
 // accumulator writes (this code, too, runs cold once per workgroup).
 __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
   bf16x8 z = bf16x8{};
-  asm volatile("" : "+v"(z));
+  asm volatile("s_nop 1" : "+v"(z));  // z was just written by VALU moves
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
@@ -685,25 +798,26 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
         }
       }
       __syncthreads();
-#pragma unroll 1
-      for (int i = 0; i < 16; ++i) {
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {  // four rows' LDS reads in flight at a time
         const int lr = 2 * i + (tid >> 7);  // row within the row block
         const int rl = 32 * rb + lr;        // row within the workgroup's block
-        if (row0 + rl >= R) break;
         f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             rd + lr * EP_ROW);
         v *= inv_s[rl];
-        if (nsplit > 1) {
-          *reinterpret_cast<f32x4*>(ws_o_ + ((gb + rl) * p.max_splits + s) * VD + d) = v;
-        } else if (OUT == OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + (gb + rl) * VD + d) = v;
-        } else {
-          bf16x4 w;
-          w[0] = (__bf16)v[0];
-          w[1] = (__bf16)v[1];
-          w[2] = (__bf16)v[2];
-          w[3] = (__bf16)v[3];
-          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out_) + (gb + rl) * VD + d) = w;
+        if (row0 + rl < R) {
+          if (nsplit > 1) {
+            *reinterpret_cast<f32x4*>(ws_o_ + ((gb + rl) * p.max_splits + s) * VD + d) = v;
+          } else if (OUT == OUT_F32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + (gb + rl) * VD + d) = v;
+          } else {
+            bf16x4 w;
+            w[0] = (__bf16)v[0];
+            w[1] = (__bf16)v[1];
+            w[2] = (__bf16)v[2];
+            w[3] = (__bf16)v[3];
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out_) + (gb + rl) * VD + d) = w;
+          }
         }
       }
     }
