@@ -46,7 +46,8 @@ extern "C" {
 typedef enum {
   TV_OK = 0,
   TV_ERR_NULL = 1,        /* a required pointer is NULL                                  */
-  TV_ERR_SHAPE = 2,       /* a size in tv_problem is out of range or inconsistent        */
+  TV_ERR_SHAPE = 2,       /* a size in tv_problem is out of range or inconsistent, or
+                             sm_scale is not positive and finite                         */
   TV_ERR_WORKSPACE = 3,   /* workspace is NULL or smaller than tv_workspace_bytes()      */
   TV_ERR_UNSUPPORTED = 4, /* out_dtype or a flags bit unknown, reserved != 0             */
   TV_ERR_INPUT = 5,       /* tv_check_inputs found a device-side precondition violated   */
@@ -116,7 +117,8 @@ size_t tv_workspace_bytes(const tv_problem* p);
  *               qo_indptr[b] .. qo_indptr[b+1]-1
  *   mask        uint8 [total_mask], nonzero = visible
  *   mask_indptr int32 [B+1]; mask_indptr[b+1] - mask_indptr[b] = n_b * L_b
- *   sm_scale    score scale (e.g. 1/sqrt(192))
+ *   sm_scale    score scale (e.g. 1/sqrt(192)); positive and finite, else
+ *               TV_ERR_SHAPE
  *   out         [total_q, H, 512] bf16 (round to nearest even) or fp32
  *   lse         fp32 [total_q, H], natural log
  *   workspace   >= tv_workspace_bytes(p) bytes, 256-byte aligned; contents on

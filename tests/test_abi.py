@@ -116,6 +116,9 @@ def test_null_pointers_and_short_workspace_fail_before_any_launch():
                                  1 << 20) == 2
     # bad problem
     assert tv.verify_attn_status(prob(num_heads=0), *args, 0.07, fake, fake, fake, 1 << 20) == 2
+    # the scale must be positive and finite (the kernels take the row max of the raw scores)
+    for bad_scale in (0.0, -0.07, float("nan"), float("inf")):
+        assert tv.verify_attn_status(p, *args, bad_scale, fake, fake, fake, 1 << 20) == 2
 
 
 def test_empty_problem_is_a_no_op():

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cstddef>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -116,6 +117,8 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   Layout lay;
   tv_status st = make_layout(p, &lay);
   if (st != TV_OK) return st;
+  // the kernels take the row max before scaling: the scale must be positive
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return TV_ERR_SHAPE;
   if (!lay.active) return TV_OK;
   if (!q || !kv_buf || !kv_indptr || !qo_indptr || !mask_indptr || !out || !lse)
     return TV_ERR_NULL;

@@ -95,11 +95,15 @@ struct SplitCtx {
   const uint32_t* wbase;    // visibility words of the block's first draft, split's first tile
   uint32_t wvoff;           // this lane's draft row offset (bytes) from wbase
   uint32_t voff;            // lane * 16: this lane's 16-byte chunk of a latent row
+  uint32_t rowb;            // 1152 (bytes per pool row) in a VGPR, the gathers' v_mad operand
+  uint32_t rp_voff;         // RoPE gather: this lane's 16-byte RoPE chunk within a pool row
+  uint32_t m_main, m_rope, m_mask;  // this wave's gather targets within a stage (bytes)
   int kbeg, kend, ntiles;   // key range [kbeg, kend) of the split, its 32-key tiles
   int wave, lane;
   // per-lane LDS offsets (relative to a stage)
-  int qk_off, pv_off, mw_off, qr_off;
+  int qk_off, pv_off, mw_off;
   int rp_off[4];
+  uint32_t al_off;          // this lane's row in a rescale-factor buffer (bytes)
   bool row_ok;
   float scale_log2;
   lds_u8* sring;            // this wave's ring of gather slots: SLOT_RING entries of 256 bytes
@@ -111,6 +115,8 @@ struct SplitCtx {
 // Their completion is tracked explicitly with vmcnt instead (nothing else in
 // the tile loop is a vector memory op).  M0 holds the LDS address; the global
 // address is an SGPR base plus a 32-bit VGPR offset, or a 64-bit VGPR address.
+// The instruction between the M0 write and the load is the one wait state that
+// write needs.
 __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -123,6 +129,37 @@ __device__ __forceinline__ void dma4_s(uint32_t voff, const void* sbase, uint32_
                : "v"(voff), "s"(sbase), "s"(m0)
                : "m0");
 }
+__device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(m0)
+               : "m0");
+}
+// Pool row gathers of a pool under 4 GiB in three instructions: M0 = stage
+// target + OFF, byte offset = slot * 1152 + lane chunk (v_mad_u32_u24: slots
+// stay below 2^24 there), 16 bytes per lane.  The slot is wave-uniform (SGPR,
+// a key's latent row) or per lane (VGPR, the RoPE chunks of 8 keys).
+template <int OFF>
+__device__ __forceinline__ void dma_row_s(uint32_t mb, int slot, const SplitCtx& c) {
+  uint32_t a;
+  asm volatile(
+      "s_add_u32 m0, %1, %2\n\t"
+      "v_mad_u32_u24 %0, %3, %4, %5\n\t"
+      "global_load_lds_dwordx4 %0, %6"
+      : "=&v"(a)
+      : "s"(mb), "n"(OFF), "s"(slot), "v"(c.rowb), "v"(c.voff), "s"(c.kv)
+      : "m0", "scc");
+}
+__device__ __forceinline__ void dma_row_v(uint32_t mb, int slot, uint32_t vo, const SplitCtx& c) {
+  uint32_t a;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "v_mad_u32_u24 %0, %2, %3, %4\n\t"
+      "global_load_lds_dwordx4 %0, %5"
+      : "=&v"(a)
+      : "s"(mb), "v"(slot), "v"(c.rowb), "v"(vo), "s"(c.kv)
+      : "m0");
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
@@ -134,10 +171,19 @@ __device__ __forceinline__ int fresh(int v) {
   return v;
 }
 
+// Register fence: as far as the compiler knows `v` is redefined here, so work
+// reading it stays below this point and work producing it stays above.  The
+// software pipeline places its steps between chosen MFMAs this way: each step
+// fences its inputs where it starts and its outputs where it ends.
+template <typename T>
+__device__ __forceinline__ void fence(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Slots of this wave's 8 keys of tile t, gathered into ring entry t % SLOT_RING
 // by one direct-to-LDS dword load (lane l: key 8*wave + (l & 7)), clamped to
 // the split's last key: keys past the split gather real, finite rows, which are
-// masked off and contribute exactly 0.  In the loop it is issued four tiles
+// masked off and contribute exactly 0.  In the loop it is issued three tiles
 // ahead, before the gathers of an earlier tile, so the vmcnt wait that makes
 // that tile readable also covers it, and the slots are then plain LDS reads: no
 // scalar load is ever pending in the tile loop (a pending one would turn every
@@ -147,83 +193,81 @@ __device__ __forceinline__ void slot_dma(const SplitCtx& c, int t) {
   dma4_s((uint32_t)k * 4u, c.idx, lds_addr(c.sring) + 256 * (t % SLOT_RING));
 }
 
-// The 8 slots as wave-uniform values, and the slot of key 8*wave + lane/8 (the
-// RoPE gather's) per lane.
-__device__ __forceinline__ void read_slots(int (&slot)[8], int& slane, const SplitCtx& c, int t) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
+// The 8 slots of a tile as wave-uniform values, and the slot of key 8*wave +
+// lane/8 (the RoPE gather's) per lane: the LDS reads (slot_load), then the
+// moves to scalar registers (slot_take, half the slots per call).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+struct SlotRaw {
+  i32x4 a, b;
+  int slane;
+};
+__device__ __forceinline__ void slot_load(SlotRaw& r, const SplitCtx& c, int t) {
   const lds_u8* e = c.sring + 256 * (t % SLOT_RING);
-  slane = *reinterpret_cast<const __attribute__((address_space(3))) int*>(
+  r.slane = *reinterpret_cast<const __attribute__((address_space(3))) int*>(
       e + 4 * (fresh(c.lane) >> 3));
-  const i32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e);
-  const i32x4 b = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e + 16);
-  slot[0] = __builtin_amdgcn_readfirstlane(a[0]);
-  slot[1] = __builtin_amdgcn_readfirstlane(a[1]);
-  slot[2] = __builtin_amdgcn_readfirstlane(a[2]);
-  slot[3] = __builtin_amdgcn_readfirstlane(a[3]);
-  slot[4] = __builtin_amdgcn_readfirstlane(b[0]);
-  slot[5] = __builtin_amdgcn_readfirstlane(b[1]);
-  slot[6] = __builtin_amdgcn_readfirstlane(b[2]);
-  slot[7] = __builtin_amdgcn_readfirstlane(b[3]);
+  r.a = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e);
+  r.b = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(e + 16);
+}
+__device__ __forceinline__ void slot_take(int (&slot)[8], SlotRaw& r, int half) {
+  i32x4& v = half ? r.b : r.a;
+  fence(v);
+  slot[4 * half + 0] = __builtin_amdgcn_readfirstlane(v[0]);
+  slot[4 * half + 1] = __builtin_amdgcn_readfirstlane(v[1]);
+  slot[4 * half + 2] = __builtin_amdgcn_readfirstlane(v[2]);
+  slot[4 * half + 3] = __builtin_amdgcn_readfirstlane(v[3]);
 }
 
-__device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0)
-               : "m0");
+// LDS targets of one stage's gathers for this wave (scalar registers).
+struct GatherDst {
+  uint32_t main, rope, mask;
+};
+__device__ __forceinline__ GatherDst gather_dst(const lds_u8* sb, const SplitCtx& c) {
+  const uint32_t a = lds_addr(sb);
+  return GatherDst{a + c.m_main, a + c.m_rope, a + c.m_mask};
 }
 
 // The DMA_PER_TILE direct-to-LDS gathers of one tile, one piece at a time.
 //   piece 0..7: latent dims 0..511 of key 8*wave + j, to stage + (8*wave + j)*ROW
-//               + key_shift(8*wave + j) = m0main + j*ROW + 16*(j >> 2);
+//               + key_shift(8*wave + j) = main + j*ROW + 16*(j >> 2);
 //   piece 8:    RoPE dims of the wave's 8 keys (one slot per 8 lanes);
 //   piece 9:    the visibility words of the tile (one per draft row).
-// WIDE: the pool may exceed 4 GiB, so the RoPE gather uses 64-bit per-lane
-// addresses; otherwise a 32-bit offset from the pool base.  The slots are
-// taken by reference to the caller's array (a pointer kept in a struct makes
-// the compiler move the array to memory).
+// WIDE: the pool may exceed 4 GiB, so the gathers use 64-bit addresses.  The
+// slots are taken by reference to the caller's array (a pointer kept in a
+// struct makes the compiler move the array to memory).
 template <bool WIDE, int J>
-__device__ __forceinline__ void gather_piece(const lds_u8* sb, const int (&slot)[8], int slane,
+__device__ __forceinline__ void gather_piece(const GatherDst& g, const int (&slot)[8], int slane,
                                              const SplitCtx& c, int t) {
   if constexpr (J < 8) {
-    const uint32_t m0 = lds_addr(sb) + 8 * c.wave * ROW + 32 * (c.wave & 1) + J * ROW +
-                        16 * (J >> 2);
-    dma16_m0(c.voff, c.kv + (int64_t)slot[J] * QK, m0);
+    constexpr int OFF = J * ROW + 16 * (J >> 2);
+    if constexpr (WIDE) dma16_m0(c.voff, c.kv + (int64_t)slot[J] * QK, g.main + OFF);
+    else dma_row_s<OFF>(g.main, slot[J], c);
   } else if constexpr (J == 8) {
-    // recomputed every tile from an opaque copy of the lane id: a hoisted,
-    // loop-invariant per-lane offset would be spilled, and its reload (a
-    // vector memory op) would wait out the gathers just issued
-    const int lane = fresh(c.lane);
-    const int k = lane >> 3;  // key 8*wave + k (slot slane), RoPE chunk slot lane & 7
-    const int s = slane;
-    const int pos = 8 * c.wave + k;
-    const uint32_t chunk = (uint32_t)((lane & 7) ^ rope_swz(pos));
-    const uint32_t m0 = lds_addr(sb) + MAIN_BYTES + 8 * c.wave * 128;
     if constexpr (WIDE) {
-      dma16_v(c.kv + (int64_t)s * QK + VD + chunk * 8, m0);
+      dma16_v(reinterpret_cast<const uint8_t*>(c.kv) + (int64_t)slane * (QK * 2) + c.rp_voff,
+              g.rope);
     } else {
-      dma16_m0((uint32_t)s * (QK * 2) + VD * 2 + chunk * 16, c.kv, m0);
+      dma_row_v(g.rope, slane, c.rp_voff, c);
     }
   } else {
-    dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1),
-           lds_addr(sb) + MAIN_BYTES + ROPE_BYTES + 256 * c.wave);
+    dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1), g.mask);
   }
 }
 
 template <bool WIDE>
-__device__ __forceinline__ void issue_tile(lds_u8* sb, const int (&slot)[8], int slane,
+__device__ __forceinline__ void issue_tile(const lds_u8* sb, const int (&slot)[8], int slane,
                                            const SplitCtx& c, int t) {
   static_assert(DMA_PER_TILE == 10, "");
-  gather_piece<WIDE, 0>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 1>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 2>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 3>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 4>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 5>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 6>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 7>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 8>(sb, slot, slane, c, t);
-  gather_piece<WIDE, 9>(sb, slot, slane, c, t);
+  const GatherDst g = gather_dst(sb, c);
+  gather_piece<WIDE, 0>(g, slot, slane, c, t);
+  gather_piece<WIDE, 1>(g, slot, slane, c, t);
+  gather_piece<WIDE, 2>(g, slot, slane, c, t);
+  gather_piece<WIDE, 3>(g, slot, slane, c, t);
+  gather_piece<WIDE, 4>(g, slot, slane, c, t);
+  gather_piece<WIDE, 5>(g, slot, slane, c, t);
+  gather_piece<WIDE, 6>(g, slot, slane, c, t);
+  gather_piece<WIDE, 7>(g, slot, slane, c, t);
+  gather_piece<WIDE, 8>(g, slot, slane, c, t);
+  gather_piece<WIDE, 9>(g, slot, slane, c, t);
 }
 
 // The MFMAs of the tile loop are inline asm: S^T accumulates in VGPRs and O^T
@@ -256,37 +300,27 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PBUF_LO = 4 * 2 * 64 * 16;  // bytes of P^T operands per tile (hi; lo follows)
 constexpr int QK_AHEAD = 4;  // LDS operand reads in flight ahead of the QK MFMA chain
-                             // (>= 4: the RoPE B operands are read inside the chain)
 
-// Q's 64 RoPE dims live in LDS (QR_ROW bytes per query row, padded so the 16
-// rows a QK read touches hit distinct banks); the 512 latent dims stay in VGPRs.
-constexpr int QR_ROW = 144;
-
-// S^T tile (32 keys x this wave's 32 rows) over all 576 dims.
-__device__ __forceinline__ f32x16 qk_tile(const lds_u8* sb, const lds_u8* qrope,
-                                          const bf16x8 (&qf)[VD / 16], const SplitCtx& c) {
-  constexpr int NK = QK / 16;  // 36 k-steps: 32 latent (B in VGPRs), 4 RoPE (B in LDS)
+// S^T tile (32 keys x this wave's 32 rows) over all 576 dims: A = key rows
+// from LDS, B = the wave's query rows, all 36 k-steps held in VGPRs.
+__device__ __forceinline__ f32x16 qk_tile(const lds_u8* sb, const bf16x8 (&qf)[QK / 16],
+                                          const SplitCtx& c) {
+  constexpr int NK = QK / 16;  // 36 k-steps: 32 latent, 4 RoPE
   const lds_u8* qa = sb + c.qk_off;
-  const lds_u8* qr = qrope + fresh(c.qr_off);
   auto a_addr = [&](int ks) -> const lds_u8* {
     return ks < VD / 16 ? qa + 32 * ks : sb + c.rp_off[ks - VD / 16];
   };
-  bf16x8 buf[QK_AHEAD], bq[4];
+  bf16x8 buf[QK_AHEAD];
 #pragma unroll
   for (int k = 0; k < QK_AHEAD; ++k) buf[k] = *reinterpret_cast<lds_bf16x8*>(a_addr(k));
   f32x16 acc;
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
     const bf16x8 a = buf[ks % QK_AHEAD];
-    const int nk = ks + QK_AHEAD;
-    if (nk < NK) {
-      buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(nk));
-      if (nk >= VD / 16)
-        bq[nk - VD / 16] = *reinterpret_cast<lds_bf16x8*>(qr + 32 * (nk - VD / 16));
-    }
-    const bf16x8 b = ks < VD / 16 ? qf[ks] : bq[ks - VD / 16];
-    if (ks == 0) mfma_first_v(acc, a, b);
-    else mfma_acc_v(acc, a, b);
+    if (ks + QK_AHEAD < NK)
+      buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(ks + QK_AHEAD));
+    if (ks == 0) mfma_first_v(acc, a, qf[ks]);
+    else mfma_acc_v(acc, a, qf[ks]);
   }
   mfma_drain_v(acc);
   return acc;
@@ -301,170 +335,240 @@ __device__ __forceinline__ uint32_t tile_mask(const lds_u8* sb, const SplitCtx& 
   return c.row_ok ? (w & valid) : 0u;
 }
 
-// Masked, scaled scores (log2 units) of the lane's 16 keys and their row max.
-__device__ __forceinline__ float scores(float (&x)[16], const f32x16& acc, uint32_t mw,
-                                        const SplitCtx& c) {
-  // register i holds key 8*(i/4) + 4*half + i%4: shift the half out once so
-  // every bit position below is a constant (per-lane masks would each hold a
-  // register for the whole loop)
-  const uint32_t mh = mw >> (4 * (c.lane >> 5));
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? acc[i] * c.scale_log2 : -INFINITY;
-    tmax = fmaxf(tmax, x[i]);
-  }
-  return fmaxf(tmax, __shfl_xor(tmax, 32));
-}
-
-// Register fence: as far as the compiler knows `v` is redefined here, so work
-// reading it stays below this point and work producing it stays above.  The
-// software pipeline below places its steps between chosen MFMAs this way.
-template <typename T>
-__device__ __forceinline__ void fence(T& v) {
-  asm volatile("" : "+v"(v));
-}
-
 // QK chain of one tile (as qk_tile) calling bg(ks) after the MFMA of each
-// k-step: work that does not depend on the chain, issued in its shadow (with
-// one wave per SIMD every instruction takes an issue slot; an MFMA keeps the
-// matrix pipe busy for about eight of them).
+// k-step: work that does not depend on the chain, issued in its shadow.  One
+// wave per SIMD issues at most one instruction every few cycles, of any kind,
+// so only about four fit beside each MFMA for free: bg work is spread thin.
 template <typename Bg>
-__device__ __forceinline__ f32x16 qk_tile_bg(const lds_u8* sb, const lds_u8* qrope,
-                                             const bf16x8 (&qf)[VD / 16], const SplitCtx& c,
-                                             Bg&& bg) {
+__device__ __forceinline__ f32x16 qk_tile_bg(const lds_u8* sb, const bf16x8 (&qf)[QK / 16],
+                                             const SplitCtx& c, Bg&& bg) {
   constexpr int NK = QK / 16;
   const lds_u8* qa = sb + c.qk_off;
-  const lds_u8* qr = qrope + fresh(c.qr_off);
   auto a_addr = [&](int ks) -> const lds_u8* {
     return ks < VD / 16 ? qa + 32 * ks : sb + c.rp_off[ks - VD / 16];
   };
-  bf16x8 buf[QK_AHEAD], bq[4];
+  bf16x8 buf[QK_AHEAD];
 #pragma unroll
   for (int k = 0; k < QK_AHEAD; ++k) buf[k] = *reinterpret_cast<lds_bf16x8*>(a_addr(k));
   f32x16 acc;
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
     const bf16x8 a = buf[ks % QK_AHEAD];
-    const int nk = ks + QK_AHEAD;
-    if (nk < NK) {
-      buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(nk));
-      if (nk >= VD / 16)
-        bq[nk - VD / 16] = *reinterpret_cast<lds_bf16x8*>(qr + 32 * (nk - VD / 16));
-    }
-    const bf16x8 b = ks < VD / 16 ? qf[ks] : bq[ks - VD / 16];
-    if (ks == 0) mfma_first_v(acc, a, b);
-    else mfma_acc_v(acc, a, b);
+    if (ks + QK_AHEAD < NK)
+      buf[ks % QK_AHEAD] = *reinterpret_cast<lds_bf16x8*>(a_addr(ks + QK_AHEAD));
+    // one LDS wait per two k-steps: the next step's operand is waited for now
+    if ((ks & 1) == 0 && ks + 1 < NK) fence(buf[(ks + 1) % QK_AHEAD]);
+    if (ks == 0) mfma_first_v(acc, a, qf[ks]);
+    else mfma_acc_v(acc, a, qf[ks]);
     bg(ks);
   }
   mfma_drain_v(acc);
   return acc;
 }
 
-// The softmax of one tile, in steps small enough to sit between MFMAs.
-// S holds S^T of the wave's 32 rows (lane l: row l%32; register i: key
-// 8*(i/4) + 4*(l/32) + i%4), mw the row's visibility word of the tile.
+// The softmax of one tile, in steps of a few instructions placed between PV
+// MFMAs.  S holds S^T of the wave's 32 rows (lane l: row l%32; register i: key
+// 8*(i/4) + 4*(l/32) + i%4) and is masked in place; mw is the row's visibility
+// word of the tile.  The probabilities stay in registers until the next tile's
+// QK chain writes them to the P buffer.
 struct Soft {
-  float x[16];  // masked, scaled scores (log2 units), then probabilities
-  float tmax, mu;
-  bf16x8 pk[2], pl[2];
+  float ma, mb, tmax;    // partial row maxima, the tile's row max (log2 units)
+  float ref0, alpha_j;   // reference before the tile, 2^(ref0 - tmax)
+  float mu;              // reference of the tile's probabilities
+  bf16x8 pk[2], pl[2];   // P^T operands of k-steps 0 and 1 (lo: precise mode)
 };
 
-constexpr int SOFT_STEPS = 9;
+// mask, max of keys 0-7, of 8-15, row max, reference x3, 8 probability pairs,
+// the P write
+constexpr int SOFT_PRE = 7;
+constexpr int SOFT_STEPS = SOFT_PRE + 8 + 1;
+
+// v_max3_f32 as written: the fmaxf library form first quiets each input (an
+// extra instruction per value); the scores are finite or -inf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 template <bool PRECISE>
+__device__ __forceinline__ void write_p(lds_u8* pb, const SplitCtx& c, const Soft& sm);
+
+// alpha_u: the LDS address of the tile's rescale factors; pb_u: its P buffer.
+template <bool PRECISE>
 __device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, uint32_t mw,
-                                          const SplitCtx& c, lds_u8* pbuf, float& m_ref,
-                                          float& l_sum, float* alpha_s, int* rflag, int t) {
-  const uint32_t mh = mw >> (4 * (c.lane >> 5));  // see scores()
-  if (step == 0 || step == 1) {
+                                          const SplitCtx& c, float& m_ref, float& l_sum,
+                                          uint32_t alpha_u, lds_u8* pb_u) {
+  if (step == 0) {
     fence(S);
+    // a tile every row of the wave sees whole (every prefix tile) skips this
+    // uniform branch; masked scores are -inf
+    if (!__all(mw == 0xffffffffu)) {
+      const uint32_t mh = mw >> (4 * (c.lane >> 5));  // constant bit positions below
 #pragma unroll
-    for (int i = 8 * step; i < 8 * step + 8; ++i) {
-      sm.x[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? S[i] * c.scale_log2 : -INFINITY;
-      fence(sm.x[i]);
+      for (int i = 0; i < 16; ++i)
+        S[i] = ((mh >> (8 * (i >> 2) + (i & 3))) & 1u) ? S[i] : -INFINITY;
     }
-  } else if (step == 2) {
-    float m = sm.x[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) m = fmaxf(m, sm.x[i]);
-    sm.tmax = fmaxf(m, __shfl_xor(m, 32));
-    fence(sm.tmax);
+    fence(S);
+  } else if (step == 1 || step == 2) {
+    fence(S);
+    const int o = 8 * (step - 1);
+    float m = max3f(S[o], S[o + 1], S[o + 2]);
+    m = max3f(m, S[o + 3], S[o + 4]);
+    m = max3f(m, S[o + 5], S[o + 6]);
+    m = max3f(m, S[o + 7], S[o + 7]);
+    if (step == 1) {
+      sm.ma = m;
+      fence(sm.ma);
+    } else {
+      sm.mb = m;
+      fence(sm.mb);
+    }
   } else if (step == 3) {
-    // first visible keys set the reference (O and l are still 0); a score more
-    // than TAU above it moves it, and l and O are scaled by 2^(old - new)
-    if (m_ref == -INFINITY) m_ref = sm.tmax;
-    const bool jump = sm.tmax > m_ref + TAU;
-    const float alpha = jump ? __builtin_amdgcn_exp2f(m_ref - sm.tmax) : 1.f;
-    if (jump) {
-      l_sum *= alpha;
-      m_ref = sm.tmax;
-    }
-    if (c.lane < 32) alpha_s[c.wave * 32 + c.lane] = alpha;
-    if (__any(jump) && c.lane == 0) rflag[t & 1] = 1;
-    // the other flag was last read in tile t-1, before this tile's first barrier
-    if (c.wave == 0 && c.lane == 0) rflag[(t + 1) & 1] = 0;
-    sm.mu = (m_ref == -INFINITY) ? 0.f : m_ref;
-    fence(sm.mu);
-  } else if (step >= 4 && step < 8) {
-#pragma unroll
-    for (int i = 4 * (step - 4); i < 4 * (step - 4) + 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(sm.x[i] - sm.mu);
-      l_sum += e;
-      sm.pk[i >> 3][i & 7] = (__bf16)e;
-      // PRECISE: the rounding residual, itself rounded to bf16 (hi + lo
-      // carries about 16 significant bits of e)
-      if (PRECISE) sm.pl[i >> 3][i & 7] = (__bf16)(e - (float)sm.pk[i >> 3][i & 7]);
-    }
+    fence(sm.mb);
+    const float m = max3f(sm.ma, sm.mb, sm.mb) * c.scale_log2;  // the scale is positive
+    // the other half of the row: v_permlane32_swap leaves, in each lane, the
+    // other half's value in one of its two results (no LDS round trip)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                     false, false);
+    sm.tmax = max3f(m, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    fence(sm.tmax);
+  } else if (step == 4) {
+    // first visible keys set the reference (O and l are still 0)
+    fence(sm.tmax);
+    sm.ref0 = (m_ref == -INFINITY) ? sm.tmax : m_ref;
+    sm.alpha_j = __builtin_amdgcn_exp2f(sm.ref0 - sm.tmax);
+    fence(sm.ref0);
+    fence(sm.alpha_j);
+  } else if (step == 5) {
+    // a score more than TAU above the reference moves it, and l and O are
+    // scaled by 2^(old - new) (alpha is exactly 1 otherwise)
+    fence(sm.alpha_j);
+    const bool jump = sm.tmax > sm.ref0 + TAU;
+    const float alpha = jump ? sm.alpha_j : 1.f;
+    l_sum *= alpha;
+    m_ref = jump ? sm.tmax : sm.ref0;
+    sm.alpha_j = alpha;
+    fence(sm.alpha_j);
     fence(l_sum);
-    fence(sm.pk[(step - 4) >> 1]);
-    if (PRECISE) fence(sm.pl[(step - 4) >> 1]);
-  } else if (step == 8) {
-    // P^T of this wave's rows: register i of lane l is key 8*(i/4) + 4*(l/32) +
-    // i%4 of row l%32, which is exactly the B operand layout of k-steps 0 (i < 8)
-    // and 1
-    typedef __attribute__((address_space(3))) bf16x8 lds_w16;
-    *reinterpret_cast<lds_w16*>(pbuf + c.wave * 2048 + c.lane * 16) = sm.pk[0];
-    *reinterpret_cast<lds_w16*>(pbuf + c.wave * 2048 + 1024 + c.lane * 16) = sm.pk[1];
+    fence(m_ref);
+  } else if (step == 6) {
+    fence(sm.alpha_j);
+    sm.mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+    // both halves of a row write the same factor: no lane masking
+    *reinterpret_cast<__attribute__((address_space(3))) float*>(
+        (uintptr_t)(alpha_u + c.al_off)) = sm.alpha_j;
+    fence(sm.mu);
+  } else if (step == SOFT_STEPS - 1) {
+    write_p<PRECISE>(pb_u, c, sm);
+  } else {
+    // probabilities i, i+1 (one packed bf16 pair), interleaved so that no
+    // exponential's result is read by the very next instruction
+    const int i = 2 * (step - SOFT_PRE);
+    float x0 = S[i], x1 = S[i + 1];
+    fence(x0);
+    fence(x1);
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c.scale_log2, -sm.mu));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c.scale_log2, -sm.mu));
+    l_sum += e0;
+    l_sum += e1;
+    fence(l_sum);
+    bf16x8& hk = sm.pk[i >> 3];
+    hk[i & 7] = (__bf16)e0;
+    hk[(i & 7) + 1] = (__bf16)e1;
+    // PRECISE: the rounding residuals, themselves rounded to bf16 (hi + lo
+    // carries about 16 significant bits of a probability)
     if (PRECISE) {
-      *reinterpret_cast<lds_w16*>(pbuf + PBUF_LO + c.wave * 2048 + c.lane * 16) = sm.pl[0];
-      *reinterpret_cast<lds_w16*>(pbuf + PBUF_LO + c.wave * 2048 + 1024 + c.lane * 16) =
-          sm.pl[1];
+      bf16x8& lk = sm.pl[i >> 3];
+      lk[i & 7] = (__bf16)(e0 - (float)hk[i & 7]);
+      lk[(i & 7) + 1] = (__bf16)(e1 - (float)hk[(i & 7) + 1]);
+      fence(lk);
     }
+    fence(hk);
+  }
+}
+
+// The PV MFMA after which each softmax step runs (32 MFMAs per tile, 64 in
+// precise mode): the first steps one per MFMA, then a probability pair every
+// third, so that each gap holds a few instructions.
+template <bool PRECISE>
+__device__ __forceinline__ constexpr int soft_at(int step) {
+  return (PRECISE ? 2 : 1) * (step < SOFT_PRE ? step : SOFT_PRE + 3 * (step - SOFT_PRE));
+}
+static_assert(soft_at<false>(SOFT_STEPS - 1) < 32 && soft_at<true>(SOFT_STEPS - 1) < 64, "");
+
+// P^T of this wave's rows into a P buffer: register i of lane l is key
+// 8*(i/4) + 4*(l/32) + i%4 of row l%32, which is exactly the B operand layout of
+// k-steps 0 (i < 8) and 1.
+template <bool PRECISE>
+__device__ __forceinline__ void write_p(lds_u8* pb, const SplitCtx& c, const Soft& sm) {
+  typedef __attribute__((address_space(3))) bf16x8 lds_w16;
+  lds_u8* w = pb + c.wave * 2048 + fresh(c.lane * 16);
+  *reinterpret_cast<lds_w16*>(w) = sm.pk[0];
+  *reinterpret_cast<lds_w16*>(w + 1024) = sm.pk[1];
+  if (PRECISE) {
+    *reinterpret_cast<lds_w16*>(w + PBUF_LO) = sm.pl[0];
+    *reinterpret_cast<lds_w16*>(w + PBUF_LO + 1024) = sm.pl[1];
   }
 }
 
 // gather_piece with the piece number known only after unrolling
 template <bool WIDE>
-__device__ __forceinline__ void gather_piece_n(int j, const lds_u8* sb, const int (&slot)[8],
+__device__ __forceinline__ void gather_piece_n(int j, const GatherDst& g, const int (&slot)[8],
                                                int slane, const SplitCtx& c, int t) {
   static_assert(DMA_PER_TILE == 10, "");
   switch (j) {
-    case 0: gather_piece<WIDE, 0>(sb, slot, slane, c, t); break;
-    case 1: gather_piece<WIDE, 1>(sb, slot, slane, c, t); break;
-    case 2: gather_piece<WIDE, 2>(sb, slot, slane, c, t); break;
-    case 3: gather_piece<WIDE, 3>(sb, slot, slane, c, t); break;
-    case 4: gather_piece<WIDE, 4>(sb, slot, slane, c, t); break;
-    case 5: gather_piece<WIDE, 5>(sb, slot, slane, c, t); break;
-    case 6: gather_piece<WIDE, 6>(sb, slot, slane, c, t); break;
-    case 7: gather_piece<WIDE, 7>(sb, slot, slane, c, t); break;
-    case 8: gather_piece<WIDE, 8>(sb, slot, slane, c, t); break;
-    default: gather_piece<WIDE, 9>(sb, slot, slane, c, t); break;
+    case 0: gather_piece<WIDE, 0>(g, slot, slane, c, t); break;
+    case 1: gather_piece<WIDE, 1>(g, slot, slane, c, t); break;
+    case 2: gather_piece<WIDE, 2>(g, slot, slane, c, t); break;
+    case 3: gather_piece<WIDE, 3>(g, slot, slane, c, t); break;
+    case 4: gather_piece<WIDE, 4>(g, slot, slane, c, t); break;
+    case 5: gather_piece<WIDE, 5>(g, slot, slane, c, t); break;
+    case 6: gather_piece<WIDE, 6>(g, slot, slane, c, t); break;
+    case 7: gather_piece<WIDE, 7>(g, slot, slane, c, t); break;
+    case 8: gather_piece<WIDE, 8>(g, slot, slane, c, t); break;
+    default: gather_piece<WIDE, 9>(g, slot, slane, c, t); break;
   }
 }
 
-// PV of tile t (stage sb), after the barrier that publishes P(t): first the O
-// rescale if some row's reference moved in this tile.
+// A operand of PV k-step kst, dim block db: V^T of 8 dims x 16 keys by two
+// transposed 8-byte reads (k-step kst covers keys 16*kst + {4*half + 0..3,
+// 8 + 4*half + 0..3}).
+__device__ __forceinline__ bf16x8 pv_a(const lds_u8* sb, const SplitCtx& c, int kst, int db) {
+  const lds_u8* va = sb + c.pv_off;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(va + (16 * kst) * ROW + 64 * db));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(va + (16 * kst + 8) * ROW + 32 + 64 * db));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
+  const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
+  return bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+}
+
+// The A operands PV reads first (dim block 0; both k-steps, or k-step 0 in
+// precise mode): they depend only on the tile, so they are read before the
+// barrier that publishes P.
 template <bool PRECISE>
-__device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds_u8* pbuf,
-                                        f32x16 (&O)[16], const float* alpha_s, const int* rflag,
-                                        int t) {
-  if (__builtin_amdgcn_readfirstlane(rflag[t & 1])) {
+__device__ __forceinline__ void pv_a_first(bf16x8 (&A0)[2], const lds_u8* sb, const SplitCtx& c) {
+  A0[0] = pv_a(sb, c, 0, 0);
+  if (!PRECISE) A0[1] = pv_a(sb, c, 1, 0);
+}
+
+// PV of tile t (stage sb), after the barrier that publishes P(t): first the O
+// rescale if some row's reference moved in this tile (resc, read ahead from the
+// tile's flag; alpha_t: its factors), then the MFMAs, each followed by bg(i)
+// (work that does not depend on them, issued in their shadow).  A0: the first
+// A operands (pv_a_first).
+template <bool PRECISE, typename Bg>
+__device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, const lds_u8* pbuf,
+                                        f32x16 (&O)[16], bool resc, const float* alpha_t,
+                                        const bf16x8 (&A0)[2], Bg&& bg) {
+  if (resc) {
     // some row's reference moved: scale this wave's O slice of every row
     // (accumulator O[4*db + rb] holds rows 32*rb + lane % 32)
     float a4[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) a4[rb] = alpha_s[32 * rb + (c.lane & 31)];
+    for (int rb = 0; rb < 4; ++rb) a4[rb] = alpha_t[32 * rb + (c.lane & 31)];
     // element by element, in place in the AGPRs: O must never have a
     // definition outside the accumulator register class in the loop
 #pragma unroll
@@ -482,19 +586,8 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds
     }
     asm volatile("s_nop 3");  // accumulator writes before the next MFMA reads them
   }
-  // O^T[dims of db, rows of rb] += V^T . P^T; k-step kst covers keys
-  // 16*kst + {4*half + 0..3, 8 + 4*half + 0..3}.  A operand (dim block db of
-  // this wave) = two transposed 8-byte reads; B operand (row block rb) = pbuf.
-  const lds_u8* va = sb + c.pv_off;
-  auto pv_a = [&](int kst, int db) -> bf16x8 {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(va + (16 * kst) * ROW + 64 * db));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(va + (16 * kst + 8) * ROW + 32 + 64 * db));
-    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo);
-    const bf16x4 h4 = __builtin_bit_cast(bf16x4, hi);
-    return bf16x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-  };
+  // O^T[dims of db, rows of rb] += V^T . P^T: A operand (dim block db of this
+  // wave) from pv_a, B operand (row block rb) from the P buffer.
   const lds_u8* pb = pbuf + fresh(c.lane * 16);
   auto pv_b = [&](int kst, int rb) -> bf16x8 {
     return *reinterpret_cast<lds_bf16x8*>(pb + rb * 2048 + kst * 1024);
@@ -505,18 +598,21 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds
     bf16x8 B[2][4], A[2][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) B[0][i] = pv_b(0, i);
-    A[0][0] = pv_a(0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) B[1][i] = pv_b(1, i);
-    A[0][1] = pv_a(1, 0);
+    A[0][0] = A0[0];
+    A[0][1] = A0[1];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int cur = db & 1;
 #pragma unroll
       for (int kst = 0; kst < 2; ++kst) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[cur][kst], B[kst][rb]);
-        if (db + 1 < 4) A[cur ^ 1][kst] = pv_a(kst, db + 1);
+        for (int rb = 0; rb < 4; ++rb) {
+          mfma_acc_a(O[4 * db + rb], A[cur][kst], B[kst][rb]);
+          bg(8 * db + 4 * kst + rb);
+        }
+        if (db + 1 < 4) A[cur ^ 1][kst] = pv_a(sb, c, kst, db + 1);
       }
     }
   } else {
@@ -530,14 +626,20 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds
         Bh[i] = pv_b(kst, i);
         Bl[i] = *reinterpret_cast<lds_bf16x8*>(pb + PBUF_LO + i * 2048 + kst * 1024);
       }
-      A[0] = pv_a(kst, 0);
+      A[0] = kst == 0 ? A0[0] : pv_a(sb, c, kst, 0);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        if (db + 1 < 4) A[(db + 1) & 1] = pv_a(kst, db + 1);
+        if (db + 1 < 4) A[(db + 1) & 1] = pv_a(sb, c, kst, db + 1);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[db & 1], Bh[rb]);
+        for (int rb = 0; rb < 4; ++rb) {
+          mfma_acc_a(O[4 * db + rb], A[db & 1], Bh[rb]);
+          bg(32 * kst + 8 * db + rb);
+        }
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) mfma_acc_a(O[4 * db + rb], A[db & 1], Bl[rb]);
+        for (int rb = 0; rb < 4; ++rb) {
+          mfma_acc_a(O[4 * db + rb], A[db & 1], Bl[rb]);
+          bg(32 * kst + 8 * db + 4 + rb);
+        }
       }
     }
   }
@@ -547,73 +649,136 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, lds
 // 0 and 1 (waited for here) and 2, then the gathers of tiles 0 and 1.
 template <bool WIDE>
 __device__ __forceinline__ void split_start(lds_u8* stages, const SplitCtx& c) {
-  int slot[8], slane;
+  int slot[8];
+  SlotRaw r;
   slot_dma(c, 0);
   slot_dma(c, 1);
   slot_dma(c, 2);
   wait_vmcnt<0>();
-  read_slots(slot, slane, c, 0);
-  issue_tile<WIDE>(stages, slot, slane, c, 0);
+  slot_load(r, c, 0);
+  slot_take(slot, r, 0);
+  slot_take(slot, r, 1);
+  issue_tile<WIDE>(stages, slot, r.slane, c, 0);
   if (c.ntiles > 1) {
-    read_slots(slot, slane, c, 1);
-    issue_tile<WIDE>(stages + STAGE, slot, slane, c, 1);
+    slot_load(r, c, 1);
+    slot_take(slot, r, 0);
+    slot_take(slot, r, 1);
+    issue_tile<WIDE>(stages + STAGE, slot, r.slane, c, 1);
   }
 }
 
-// All tiles of the split after split_start, software-pipelined: iteration t
-// runs QK of tile t+1 with, in the shadow of its MFMAs, the gathers of tile t+2
-// (and the slots of t+3) and the softmax of tile t; then, after the barrier
-// that publishes P(t), the PV of tile t.  Tile k sits in stage k % 3: at
-// iteration t stage t (PV), t+1 (QK) and t+2 (being gathered).  Every gather
-// issued before iteration t's barrier has landed by then (vmcnt(0): the
-// iteration issues nothing else to global memory).
+// Whether some row's reference moved in a tile: its rescale factors (alpha_t,
+// 128 rows) are not all exactly 1.
+__device__ __forceinline__ void alpha_load(float& a0, float& a1, const float* alpha_t,
+                                           const SplitCtx& c) {
+  a0 = alpha_t[c.lane];
+  a1 = alpha_t[c.lane + 64];
+}
+__device__ __forceinline__ int alpha_moved(float a0, float a1) {
+  return __any(a0 != 1.f || a1 != 1.f) ? 1 : 0;
+}
+
+// Iteration t's QK chain (tile t+1, stage nx1) with, in its shadow: the read
+// of tile t's rescale factors; if GATHER, the slots and gathers of tile t+2
+// (stage nx2) and the slots of tile t+3; then tile t+1's visibility words and
+// the first PV operands of tile t (stage cur).
+template <bool WIDE, bool PRECISE, bool GATHER>
+__device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
+                                           const bf16x8 (&qf)[QK / 16], const float* alpha_t,
+                                           int t, int cur, int nx1, int nx2, uint32_t& mw,
+                                           int& resc, bf16x8 (&A0)[2]) {
+  constexpr int G0 = 5;  // first gather piece; then one every third k-step
+  static_assert(G0 + 3 * (DMA_PER_TILE - 1) + 2 < QK / 16, "");
+  SlotRaw r;
+  int slot[8];
+  float a0, a1;
+  const GatherDst g = gather_dst(stages + nx2 * STAGE, c);
+  auto bg = [&](int ks) {
+    if (ks == 0) {
+      if (GATHER) {
+        slot_load(r, c, t + 2);
+        slot_dma(c, t + 3);
+      }
+    } else if (ks == 1) {
+      alpha_load(a0, a1, alpha_t, c);
+    } else if (ks == 2 || ks == 3) {
+      if (GATHER) slot_take(slot, r, ks - 2);
+    } else if (ks == 4) {
+      fence(a0);
+      fence(a1);
+      resc = alpha_moved(a0, a1);
+    } else if (ks >= G0 && ks < G0 + 3 * DMA_PER_TILE && (ks - G0) % 3 == 0) {
+      if (GATHER) gather_piece_n<WIDE>((ks - G0) / 3, g, slot, r.slane, c, t + 2);
+    } else if (ks == G0 + 3 * DMA_PER_TILE - 2) {
+      mw = tile_mask(stages + nx1 * STAGE, c, t + 1);
+    } else if (ks == G0 + 3 * DMA_PER_TILE - 1) {
+      pv_a_first<PRECISE>(A0, stages + cur * STAGE, c);
+    }
+  };
+  return qk_tile_bg(stages + nx1 * STAGE, qf, c, bg);
+}
+
+// All tiles of the split after split_start, software-pipelined, one barrier per
+// tile.  Tile k sits in stage k % 3, its P in P buffer k % 2 and its rescale
+// factors in alpha_s[k % 2].  Iteration t, after its barrier, runs the QK chain
+// of tile t+1 (qk_phase: the gathers of tile t+2 in its shadow), then the PV of
+// tile t with, in its shadow, the softmax of tile t+1, which ends by writing
+// P(t+1) and tile t+1's factors.  The barrier of iteration t publishes tile
+// t+1's gathers (every gather issued before it has landed: vmcnt(0), the
+// iteration issues nothing else to global memory), P(t) and tile t's factors,
+// and frees stage t-1, P buffer t-1 and factors t-1 for reuse.  The softmax of
+// tile 0 runs ahead of the loop.
 template <bool WIDE, bool PRECISE>
-__device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, const lds_u8* qrope,
-                                          lds_u8* pbuf, const bf16x8 (&qf)[VD / 16],
-                                          f32x16 (&O)[16], float& m_ref, float& l_sum,
-                                          float* alpha_s, int* rflag) {
+__device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds_u8* pbuf,
+                                          const bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
+                                          float& m_ref, float& l_sum, float* alpha_s) {
+  constexpr int PB = PRECISE ? 2 * PBUF_LO : PBUF_LO;  // bytes of one P buffer
   const int nt = c.ntiles;
-  // tile 0: its gathers landed (only tile 1's may be outstanding), QK
+  const uint32_t alpha_lds = lds_addr((lds_u8*)alpha_s);
+  // tile 0: its gathers landed (only tile 1's may be outstanding), QK, softmax
   if (nt > 1) wait_vmcnt<DMA_PER_TILE>();
   else wait_vmcnt<0>();
   __syncthreads();
-  uint32_t mw = tile_mask(stages, c, 0);
-  f32x16 S = qk_tile(stages, qrope, qf, c);
+  Soft sm;
+  {
+    f32x16 S = qk_tile(stages, qf, c);
+    const uint32_t mw = tile_mask(stages, c, 0);
+#pragma unroll
+    for (int st = 0; st < SOFT_STEPS; ++st)
+      soft_step<PRECISE>(st, sm, S, mw, c, m_ref, l_sum, alpha_lds, pbuf);
+  }
   int cur = 0;  // stage of tile t
   for (int t = 0; t < nt; ++t) {
     const int nx1 = cur == NSTAGE - 1 ? 0 : cur + 1;  // stage of tile t+1
     const int nx2 = cur == 0 ? NSTAGE - 1 : cur - 1;  // stage of tile t+2
     if (t + 1 < nt) wait_vmcnt<0>();
-    __syncthreads();  // tile t+1 readable; every wave is done with PV(t-1)
-    Soft sm;
-    uint32_t mw_next = 0;
-    int slot[8], slane = 0;
-    const bool gather = t + 2 < nt;
-    auto bg = [&](int ks) {
-      if (ks == 0) {
-        if (gather) read_slots(slot, slane, c, t + 2);
-        slot_dma(c, t + 3);
-      } else if (ks <= DMA_PER_TILE) {
-        if (gather) gather_piece_n<WIDE>(ks - 1, stages + nx2 * STAGE, slot, slane, c, t + 2);
-      } else if (ks == DMA_PER_TILE + 1) {
-        if (t + 1 < nt) mw_next = tile_mask(stages + nx1 * STAGE, c, t + 1);
-      } else if (ks >= 12 && ks < 12 + 2 * SOFT_STEPS && (ks & 1) == 0) {
-        soft_step<PRECISE>((ks - 12) >> 1, sm, S, mw, c, pbuf, m_ref, l_sum, alpha_s, rflag, t);
-      }
-    };
-    f32x16 S_next;
-    if (t + 1 < nt) {
-      S_next = qk_tile_bg(stages + nx1 * STAGE, qrope, qf, c, bg);
+    __syncthreads();
+    const float* alpha_t = alpha_s + ROWS_PER_WG * (t & 1);
+    f32x16 S;
+    uint32_t mw = 0;  // tile t+1's visibility (none past the last tile)
+    int resc;         // some row's reference moved in tile t
+    bf16x8 A0[2];
+    if (t + 2 < nt) {
+      S = qk_phase<WIDE, PRECISE, true>(stages, c, qf, alpha_t, t, cur, nx1, nx2, mw, resc, A0);
+    } else if (t + 1 < nt) {
+      S = qk_phase<WIDE, PRECISE, false>(stages, c, qf, alpha_t, t, cur, nx1, nx2, mw, resc,
+                                         A0);
     } else {
-      // last tile: nothing left to hide the softmax behind
-#pragma unroll
-      for (int st = 0; st < SOFT_STEPS; ++st)
-        soft_step<PRECISE>(st, sm, S, mw, c, pbuf, m_ref, l_sum, alpha_s, rflag, t);
+      float a0, a1;
+      alpha_load(a0, a1, alpha_t, c);
+      pv_a_first<PRECISE>(A0, stages + cur * STAGE, c);
+      resc = alpha_moved(a0, a1);
+      S = f32x16{};  // a tile past the end: its softmax below masks it off whole
     }
-    __syncthreads();  // P(t) of all 128 rows is in pbuf, rflag and alpha_s are set
-    pv_tile<PRECISE>(stages + cur * STAGE, c, pbuf, O, alpha_s, rflag, t);
-    S = S_next;
-    mw = mw_next;
+    const uint32_t alpha_n = alpha_lds + 4 * ROWS_PER_WG * ((t + 1) & 1);
+    lds_u8* pb_n = pbuf + PB * ((t + 1) & 1);
+    pv_tile<PRECISE>(stages + cur * STAGE, c, pbuf + PB * (t & 1), O, resc != 0, alpha_t, A0,
+                     [&](int i) {
+#pragma unroll
+                       for (int st = 0; st < SOFT_STEPS; ++st)
+                         if (i == soft_at<PRECISE>(st))
+                           soft_step<PRECISE>(st, sm, S, mw, c, m_ref, l_sum, alpha_n, pb_n);
+                     });
     cur = nx1;
   }
   // drain: no gather may still be writing LDS when the epilogue reuses it
@@ -639,14 +804,11 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     void* __restrict__ out_, float* __restrict__ lse_, float* __restrict__ ws_o_,
     float* __restrict__ ws_lse_, SplitScalars p) {
   __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t qrope_s[ROWS_PER_WG * QR_ROW];
-  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[PRECISE ? 2 * PBUF_LO : PBUF_LO];
+  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[2 * (PRECISE ? 2 * PBUF_LO : PBUF_LO)];
   __shared__ float inv_s[ROWS_PER_WG];
   __shared__ __attribute__((aligned(1024))) uint8_t sring_s[4 * SLOT_RING * 256];
-  __shared__ float alpha_s[ROWS_PER_WG];
-  __shared__ int rflag_s[2];
+  __shared__ float alpha_s[2 * ROWS_PER_WG];
   lds_u8* const stages = (lds_u8*)stages_s;
-  lds_u8* const qrope = (lds_u8*)qrope_s;
   lds_u8* const pbuf = (lds_u8*)pbuf_s;
 
   const int tid = threadIdx.x;
@@ -697,6 +859,12 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   c.wbase = mask_words_ + (int64_t)(q0 + i0) * p.max_tiles + c.kbeg / TILE;
   c.wvoff = (uint32_t)min(64 * wave + lane, nd - 1) * (uint32_t)p.max_tiles * 4u;
   c.voff = (uint32_t)lane * 16u;
+  asm volatile("v_mov_b32 %0, 0x480" : "=v"(c.rowb));  // QK * 2, kept in a register
+  c.rp_voff = VD * 2 + 16 * ((lane & 7) ^ rope_swz(8 * wave + (lane >> 3)));
+  c.m_main = 8 * wave * ROW + 32 * (wave & 1);
+  c.m_rope = MAIN_BYTES + 8 * wave * 128;
+  c.m_mask = MAIN_BYTES + ROPE_BYTES + 256 * wave;
+  c.al_off = 4 * (wave * 32 + l32);
 
   // per-lane LDS read offsets (relative to a stage)
   c.qk_off = l32 * ROW + key_shift(l32) + 16 * half;  // + 32*ks: latent chunk 2*ks + half
@@ -719,34 +887,23 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   // their memory latency overlaps the loads below
   if (c.ntiles > 0) split_start<WIDE>(stages, c);
 
-  // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7): the 512
-  // latent dims into VGPRs, the 64 RoPE dims of all 128 rows into LDS.  A row
-  // past the request's rows uses the block's first row instead: its scores stay
-  // in its own lane, are masked off, and it writes nothing.
-  bf16x8 qf[VD / 16];
+  // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7), all 576
+  // dims in VGPRs for the whole split.  A row past the request's rows uses the
+  // block's first row instead: its scores stay in its own lane, are masked
+  // off, and it writes nothing.
+  bf16x8 qf[QK / 16];
   {
     const int64_t gq = c.row_ok ? g : (int64_t)q0 * H + row0;
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_ + gq * QK + half * 8);
 #pragma unroll
-    for (int ks = 0; ks < VD / 16; ++ks) qf[ks] = qp[2 * ks];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int id = tid + 256 * k;  // 128 rows x 8 RoPE chunks
-      const int rl = id >> 3, ch = id & 7;
-      const int64_t gr = (int64_t)q0 * H + (row0 + rl < R ? row0 + rl : row0);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(q_ + gr * QK + VD + ch * 8);
-      *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(qrope + rl * QR_ROW + ch * 16) = v;
-    }
+    for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = qp[2 * ks];
   }
-  c.qr_off = (wave * 32 + l32) * QR_ROW + 16 * half;  // + 32*j: RoPE chunk 2*j + half
   // every Q load has landed before the tile loop (an asm use of each register
   // makes the compiler wait here): otherwise it keeps the qf registers pending
   // at the loop header and puts a vmcnt wait before each QK MFMA, which in
   // steady state waits out the tile gathers instead
 #pragma unroll
-  for (int ks = 0; ks < VD / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
-  if (tid < 2) rflag_s[tid] = 0;
-  __syncthreads();
+  for (int ks = 0; ks < QK / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
   // 4*(l/32) + r%4) and rows 32*rb + l%32: accumulator O[4*db + rb]
@@ -755,7 +912,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
   if (c.ntiles > 0)
-    run_split<WIDE, PRECISE>(stages, c, qrope, pbuf, qf, O, m_ref, l_sum, alpha_s, rflag_s);
+    run_split<WIDE, PRECISE>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s);
 
   // the last PV MFMAs must finish before O is read out of the AGPRs
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
