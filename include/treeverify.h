@@ -58,11 +58,13 @@ typedef enum {
 typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
 
 /* tv_problem.flags.  The softmax probabilities (fp32) enter the P.V product on
- * the bf16 matrix cores.  By default each is rounded once to bf16, which bounds
- * the output error by 2^-8 * max |v| over the row's visible keys.
- * TV_FLAG_PRECISE_P splits each probability into two bf16 terms (hi + lo, about
- * 16 significant bits) and runs the P.V product on both: the error bound
- * becomes 2^-16 * max |v| for 32 more MFMAs per 32-key tile (68 -> 100).
+ * the bf16 matrix cores.  By default each is rounded once to bf16, and a split's
+ * partial output is kept as fp16 under an exact power-of-two scale; together
+ * these bound the output error by (2^-8 + 2^-11) * max |v| over the row's
+ * visible keys.  TV_FLAG_PRECISE_P splits each probability into two bf16 terms
+ * (hi + lo, about 16 significant bits), runs the P.V product on both and keeps
+ * fp32 partial outputs: the bound becomes about 2^-16 * max |v|, for 32 more
+ * MFMAs per 32-key tile (68 -> 100) and twice the partial-output traffic.
  * Meant for value distributions with large outliers. */
 #define TV_FLAG_PRECISE_P 1
 
@@ -102,7 +104,9 @@ tv_status tv_get_plan(const tv_problem* p, tv_plan* plan);
 /* Bytes of device workspace tv_verify_attn needs for `p` (0 if `p` is invalid
  * or there is nothing to compute).  It holds one 32-bit visibility word per
  * (draft token, 32-key tile) and, when more than one split is used, the
- * per-split partial outputs (total_q * H * max_splits * (512 + 1) fp32). */
+ * per-split partial outputs: total_q * H * max_splits entries of 512 fp16 values
+ * plus two fp32 (lse, scale exponent), or with TV_FLAG_PRECISE_P of 512 + 1 fp32,
+ * each part rounded up to 256 bytes. */
 size_t tv_workspace_bytes(const tv_problem* p);
 
 /*

@@ -14,13 +14,18 @@ MEAN_REL = 2e-3
 
 
 def p_rounding_bound(w: W.Workload, precise: bool):
-    """Per value dim, the most the rounding of the probabilities to bf16 can move
-    an output: sum_j |p~_j - p_j| |v_jd| / sum_j p_j <= u * max_j |v_jd| with
-    u = 2^-8 (one bf16 rounding: 8 significant bits) or 2^-16 (hi + lo pair), max over the
-    pool rows any request references."""
+    """Per value dim, the most the kernels' deliberate roundings can move an
+    output, as u * max_j |v_jd| over the pool rows any request references.
+    Probabilities rounded to bf16 move it by sum_j |p~_j - p_j| |v_jd| / sum_j p_j
+    <= 2^-8 max_j |v_jd| (8 significant bits), or 2^-16 as a hi + lo pair (precise
+    mode).  Without precise mode the partial outputs of a split are also stored as
+    fp16 (11 significant bits) under an exact power-of-two scale: each is a convex
+    combination of value rows, so that adds at most 2^-11 max_j |v_jd| (fp32
+    partials in precise mode add nothing at this scale)."""
     v = W.bf16_to_f32(w.kv[np.unique(w.kv_indices)][:, :512]) if w.kv_indices.size else \
         np.zeros((1, 512), np.float32)
-    return (2.0 ** (-16 if precise else -8)) * np.abs(v).max(axis=0).astype(np.float64)
+    u = 2.0 ** -16 if precise else 2.0 ** -8 + 2.0 ** -11
+    return u * np.abs(v).max(axis=0).astype(np.float64)
 
 
 def torch_mod():

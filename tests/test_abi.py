@@ -58,9 +58,15 @@ def test_plan_explicit_splits_cover_the_longest_request():
     assert pl["max_splits"] <= 32 and pl["merge"] == 1 and pl["row_blocks"] == 4
     rows = 32 * 16
     words = -(-(32 * 1025 * 4) // 256) * 256
-    parts = -(-(rows * pl["max_splits"] * 512 * 4) // 256) * 256 + \
-        -(-(rows * pl["max_splits"] * 4) // 256) * 256
-    assert pl["workspace_bytes"] == words + parts
+
+    def parts(out_bytes, lse_bytes):
+        return -(-(rows * pl["max_splits"] * 512 * out_bytes) // 256) * 256 + \
+            -(-(rows * pl["max_splits"] * lse_bytes) // 256) * 256
+    # default: fp16 partial outputs, (lse, scale exponent) per (row, split)
+    assert pl["workspace_bytes"] == words + parts(2, 8)
+    # precise: fp32 partial outputs, the lse alone
+    p.flags = tv.FLAG_PRECISE_P
+    assert tv.plan(p)["workspace_bytes"] == words + parts(4, 4)
 
 
 @pytest.mark.parametrize("k", [1, 2, 4, 7, 16, 64, 128, 1000, 5000])
@@ -95,8 +101,15 @@ def test_bad_shapes_are_rejected():
     with pytest.raises(tv.TreeVerifyError) as e:
         tv.plan(bad)
     assert e.value.code == 4
-    # the precise-probability flag changes no plan or workspace arithmetic
-    assert tv.plan(prob(flags=tv.FLAG_PRECISE_P)) == tv.plan(prob())
+    # the precise-probability flag keeps the split plan; its partial outputs are
+    # fp32 instead of scaled fp16, so a merging plan needs more workspace
+    pp, pd = tv.plan(prob(flags=tv.FLAG_PRECISE_P)), tv.plan(prob())
+    assert {k: v for k, v in pp.items() if k != "workspace_bytes"} == \
+        {k: v for k, v in pd.items() if k != "workspace_bytes"}
+    many = dict(max_kv_len=40000, total_kv=40000, num_splits=8)
+    assert tv.plan(prob(**many))["merge"]
+    assert tv.workspace_bytes(prob(flags=tv.FLAG_PRECISE_P, **many)) > \
+        tv.workspace_bytes(prob(**many))
 
 
 def test_null_pointers_and_short_workspace_fail_before_any_launch():

@@ -89,12 +89,15 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   lay->words_bytes = align256(p->total_q * lay->max_tiles * 4);
   int64_t off = lay->words_bytes;
   if (max_splits > 1) {
+    // partial outputs: fp32 in precise mode, else fp16 with a scale exponent
+    // stored beside each partial lse
+    const bool f16_parts = (p->flags & TV_FLAG_PRECISE_P) == 0;
     const int64_t prow = p->total_q * p->num_heads * max_splits;
     lay->wso_off = off;
-    lay->wso_bytes = align256(prow * TV_V_DIM * 4);
+    lay->wso_bytes = align256(prow * TV_V_DIM * (f16_parts ? 2 : 4));
     off += lay->wso_bytes;
     lay->wsl_off = off;
-    lay->wsl_bytes = align256(prow * 4);
+    lay->wsl_bytes = align256(prow * (f16_parts ? 8 : 4));
     off += lay->wsl_bytes;
   }
   lay->plan.split_keys = (int32_t)split_keys;
@@ -156,7 +159,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.mask_words = words;
   sp.out = out;
   sp.lse = lse;
-  sp.ws_o = lay.plan.merge ? reinterpret_cast<float*>(ws + lay.wso_off) : nullptr;
+  sp.ws_o = lay.plan.merge ? static_cast<void*>(ws + lay.wso_off) : nullptr;
   sp.ws_lse = lay.plan.merge ? reinterpret_cast<float*>(ws + lay.wsl_off) : nullptr;
   sp.s.scale_log2 = (float)((double)sm_scale * 1.4426950408889634074);
   sp.s.num_heads = p->num_heads;
@@ -184,7 +187,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     mp.split_keys = lay.plan.split_keys;
     mp.max_splits = lay.plan.max_splits;
     const int64_t gx = (int64_t)p->max_q_len * p->num_heads;  // one row per workgroup
-    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, s) != hipSuccess)
+    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, s) != hipSuccess)
       return TV_ERR_LAUNCH;
   }
   return TV_OK;

@@ -10,6 +10,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int QK = 576;           // key / query dims (512 latent + 64 RoPE)
@@ -47,8 +49,12 @@ struct SplitParams {
   const uint32_t* mask_words; // [total_q, max_tiles] from tv_pack_mask_kernel
   void* out;                  // [total_q, H, 512] bf16 or fp32 (requests with one split)
   float* lse;                 // [total_q, H]
-  float* ws_o;                // [total_q * H, max_splits, 512] fp32 partial outputs
-  float* ws_lse;              // [total_q * H, max_splits] fp32 partial lse (natural log)
+  // partial outputs [total_q * H, max_splits, 512]: fp32 in precise mode, else
+  // fp16 scaled by a power of two per (row, split)
+  void* ws_o;
+  // per (row, split): the partial lse (natural log), fp32; without precise mode
+  // followed by the scale exponent k (as a float): o = h * 2^k
+  float* ws_lse;
   SplitScalars s;
   bool wide;                  // pool larger than 4 GiB: 64-bit gather addresses
   bool precise;               // probabilities as bf16 hi + lo in the P.V product
@@ -57,8 +63,8 @@ struct SplitParams {
 struct MergeParams {
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;
-  const float* ws_o;
-  const float* ws_lse;
+  const void* ws_o;           // as SplitParams::ws_o
+  const float* ws_lse;        // as SplitParams::ws_lse
   void* out;
   float* lse;
   int32_t num_heads;
@@ -68,6 +74,7 @@ struct MergeParams {
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st);
 hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st);
-hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
+                        hipStream_t st);
 
 }  // namespace tv

@@ -375,13 +375,15 @@ struct Soft {
   float ma, mb, tmax;    // partial row maxima, the tile's row max (log2 units)
   float ref0, alpha_j;   // reference before the tile, 2^(ref0 - tmax)
   float mu;              // reference of the tile's probabilities
+  float y0, y1, e0, e1;  // a probability pair: exponents, then values
   bf16x8 pk[2], pl[2];   // P^T operands of k-steps 0 and 1 (lo: precise mode)
 };
 
-// mask, max of keys 0-7, of 8-15, row max, reference x3, 8 probability pairs,
-// the P write
+// mask, max of keys 0-7, of 8-15, row max, reference x3, 8 probability pairs
+// in three steps each (exponents, exponentials, sum and bf16 pair), the P write:
+// one step per PV MFMA
 constexpr int SOFT_PRE = 7;
-constexpr int SOFT_STEPS = SOFT_PRE + 8 + 1;
+constexpr int SOFT_STEPS = SOFT_PRE + 3 * 8 + 1;
 
 // v_max3_f32 as written: the fmaxf library form first quiets each input (an
 // extra instruction per value); the scores are finite or -inf.
@@ -462,38 +464,48 @@ __device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, uint32_
   } else if (step == SOFT_STEPS - 1) {
     write_p<PRECISE>(pb_u, c, sm);
   } else {
-    // probabilities i, i+1 (one packed bf16 pair), interleaved so that no
-    // exponential's result is read by the very next instruction
-    const int i = 2 * (step - SOFT_PRE);
-    float x0 = S[i], x1 = S[i + 1];
-    fence(x0);
-    fence(x1);
-    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c.scale_log2, -sm.mu));
-    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c.scale_log2, -sm.mu));
-    l_sum += e0;
-    l_sum += e1;
-    fence(l_sum);
-    bf16x8& hk = sm.pk[i >> 3];
-    hk[i & 7] = (__bf16)e0;
-    hk[(i & 7) + 1] = (__bf16)e1;
-    // PRECISE: the rounding residuals, themselves rounded to bf16 (hi + lo
-    // carries about 16 significant bits of a probability)
-    if (PRECISE) {
-      bf16x8& lk = sm.pl[i >> 3];
-      lk[i & 7] = (__bf16)(e0 - (float)hk[i & 7]);
-      lk[(i & 7) + 1] = (__bf16)(e1 - (float)hk[(i & 7) + 1]);
-      fence(lk);
+    // probabilities i, i+1 (one packed bf16 pair)
+    const int j = step - SOFT_PRE, i = 2 * (j / 3);
+    if (j % 3 == 0) {
+      float x0 = S[i], x1 = S[i + 1];
+      fence(x0);
+      fence(x1);
+      sm.y0 = __builtin_fmaf(x0, c.scale_log2, -sm.mu);
+      sm.y1 = __builtin_fmaf(x1, c.scale_log2, -sm.mu);
+      fence(sm.y0);
+      fence(sm.y1);
+    } else if (j % 3 == 1) {
+      fence(sm.y1);
+      sm.e0 = __builtin_amdgcn_exp2f(sm.y0);
+      sm.e1 = __builtin_amdgcn_exp2f(sm.y1);
+      fence(sm.e0);
+      fence(sm.e1);
+    } else {
+      fence(sm.e1);
+      l_sum += sm.e0;
+      l_sum += sm.e1;
+      fence(l_sum);
+      bf16x8& hk = sm.pk[i >> 3];
+      hk[i & 7] = (__bf16)sm.e0;
+      hk[(i & 7) + 1] = (__bf16)sm.e1;
+      // PRECISE: the rounding residuals, themselves rounded to bf16 (hi + lo
+      // carries about 16 significant bits of a probability)
+      if (PRECISE) {
+        bf16x8& lk = sm.pl[i >> 3];
+        lk[i & 7] = (__bf16)(sm.e0 - (float)hk[i & 7]);
+        lk[(i & 7) + 1] = (__bf16)(sm.e1 - (float)hk[(i & 7) + 1]);
+        fence(lk);
+      }
+      fence(hk);
     }
-    fence(hk);
   }
 }
 
-// The PV MFMA after which each softmax step runs (32 MFMAs per tile, 64 in
-// precise mode): the first steps one per MFMA, then a probability pair every
-// third, so that each gap holds a few instructions.
+// The PV MFMA after which each softmax step runs: one step per MFMA (32 per
+// tile), or per second MFMA in precise mode (64).
 template <bool PRECISE>
 __device__ __forceinline__ constexpr int soft_at(int step) {
-  return (PRECISE ? 2 : 1) * (step < SOFT_PRE ? step : SOFT_PRE + 3 * (step - SOFT_PRE));
+  return (PRECISE ? 2 : 1) * step;
 }
 static_assert(soft_at<false>(SOFT_STEPS - 1) < 32 && soft_at<true>(SOFT_STEPS - 1) < 64, "");
 
@@ -786,6 +798,35 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
   __syncthreads();
 }
 
+// Epilogue helpers.  O^T of row block RB (accumulators O[4*db + RB]) into the
+// staging region of this lane's row: dims 32*db + 8*(r/4) + 4*half + r%4.
+template <int RB>
+__device__ __forceinline__ void stage_rows(lds_u8* ep, const f32x16 (&O)[16]) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& o = O[4 * db + RB];
+      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(ep + 128 * db + 32 * q) =
+          f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+__device__ __forceinline__ f16x8 to_f16x8(const f32x4& a, const f32x4& b) {
+  return f16x8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
+               (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& a, const f32x4& b) {
+  return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+}
+
 // O = 0 by MFMAs with zero operands: 16 instructions instead of 256
 // accumulator writes (this code, too, runs cold once per workgroup).
 __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
@@ -801,7 +842,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
     const int32_t* __restrict__ qo_indptr_, const uint32_t* __restrict__ mask_words_,
-    void* __restrict__ out_, float* __restrict__ lse_, float* __restrict__ ws_o_,
+    void* __restrict__ out_, float* __restrict__ lse_, void* __restrict__ ws_o_,
     float* __restrict__ ws_lse_, SplitScalars p) {
   __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[2 * (PRECISE ? 2 * PBUF_LO : PBUF_LO)];
@@ -927,54 +968,84 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   if (half == 0) inv_s[wave * 32 + l32] = empty ? 0.f : 1.f / l_tot;
   if (c.row_ok && half == 0) {
     if (nsplit == 1) lse_[g] = lse_nat;
-    else ws_lse_[g * p.max_splits + s] = lse_nat;
+    else if (PRECISE) ws_lse_[g * p.max_splits + s] = lse_nat;
+    else ws_lse_[2 * (g * p.max_splits + s)] = lse_nat;  // the scale exponent follows
   }
   __syncthreads();
 
   // O^T -> LDS -> global, one row block (32 rows) at a time: wave w puts its
-  // 128 dims of the 32 rows into region w ([32 rows][EP_ROW bytes]); then each
-  // row is stored as one contiguous run by 128 threads (a small rolled loop:
-  // like the rest of the kernel this code runs cold once per workgroup).
+  // 128 dims of the 32 rows into region w ([32 rows][EP_ROW bytes]); then 8
+  // lanes store each row: lane i of a row covers dims 64k + 8i .. +7, k = 0..7,
+  // so that each store instruction writes whole contiguous row segments.  The
+  // row-block loop is rolled (this code runs once per workgroup).
   constexpr int EP_ROW = 528;  // 512 bytes of a row's 128 dims, + 16: conflict-free writes
   static_assert(4 * 32 * EP_ROW <= NSTAGE * STAGE, "");
   {
     lds_u8* ep = stages + wave * 32 * EP_ROW + l32 * EP_ROW + 16 * half;
-    const int64_t gb = (int64_t)q0 * H + row0;  // global row of the block's first row
-    const int d = 4 * (tid & 127);              // this thread's dims in the store loop
-    const lds_u8* rd = stages + (d >> 7) * 32 * EP_ROW + (d & 127) * 4;
-#pragma unroll
+    const int lr = tid >> 3, si = tid & 7;       // row within the row block, lane in the row
+    const lds_u8* rd = stages + lr * EP_ROW + 32 * si;  // dims 8*si of chunk k = 0
+#pragma unroll 1
     for (int rb = 0; rb < 4; ++rb) {
       if (rb > 0) __syncthreads();  // the previous row block has been read back
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16& o = O[4 * db + rb];
-          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(ep + 128 * db + 32 * q) =
-              f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-        }
+      switch (rb) {
+        case 0: stage_rows<0>(ep, O); break;
+        case 1: stage_rows<1>(ep, O); break;
+        case 2: stage_rows<2>(ep, O); break;
+        default: stage_rows<3>(ep, O); break;
       }
       __syncthreads();
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {  // four rows' LDS reads in flight at a time
-        const int lr = 2 * i + (tid >> 7);  // row within the row block
-        const int rl = 32 * rb + lr;        // row within the workgroup's block
-        f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            rd + lr * EP_ROW);
-        v *= inv_s[rl];
-        if (row0 + rl < R) {
-          if (nsplit > 1) {
-            *reinterpret_cast<f32x4*>(ws_o_ + ((gb + rl) * p.max_splits + s) * VD + d) = v;
-          } else if (OUT == OUT_F32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out_) + (gb + rl) * VD + d) = v;
-          } else {
-            bf16x4 w;
-            w[0] = (__bf16)v[0];
-            w[1] = (__bf16)v[1];
-            w[2] = (__bf16)v[2];
-            w[3] = (__bf16)v[3];
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out_) + (gb + rl) * VD + d) = w;
+      const int rl = 32 * rb + lr;  // row within the workgroup's block
+      // chunk k: dims 64k + 8*si: region k/2, byte offset 256*(k&1) + 32*si
+      f32x4 x[16];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const lds_u8* c0 = rd + (k >> 1) * 32 * EP_ROW + 256 * (k & 1);
+        x[2 * k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(c0);
+        x[2 * k + 1] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(c0 + 16);
+      }
+      float inv = inv_s[rl];
+      const int64_t gr = (int64_t)q0 * H + row0 + rl;
+      const bool live = row0 + rl < R;
+      if (nsplit > 1 && !PRECISE) {
+        // fp16 partial with an exact power-of-two scale per row: with the
+        // row's max |o| < 2^e, o * 2^(15 - e) stays below 2^15 (no overflow,
+        // values down to 2^-29 of the max stay normal); o = h * 2^(e - 15).
+        // The scale folds into the 1/l multiply.
+        float m = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          m = max3f(m, max3f(fabsf(x[k][0]), fabsf(x[k][1]), fabsf(x[k][2])), fabsf(x[k][3]));
+        float d = dpp_f<0xb1>(m);  // the 8 lanes of the row: pairs, quads, halves of 8
+        m = max3f(m, d, d);
+        d = dpp_f<0x4e>(m);
+        m = max3f(m, d, d);
+        d = dpp_f<0x141>(m);
+        m = max3f(m, d, d);
+        const int e = __builtin_amdgcn_frexp_expf(m * inv);
+        inv = __builtin_ldexpf(inv, 15 - e);
+        if (live) {
+          const int64_t wi = gr * p.max_splits + s;
+          _Float16* o = static_cast<_Float16*>(ws_o_) + wi * VD + 8 * si;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<f16x8*>(o + 64 * k) = to_f16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
+          if (si == 0) ws_lse_[2 * wi + 1] = (float)(e - 15);
+        }
+      } else if (live) {
+        if (nsplit > 1 || OUT == OUT_F32) {
+          float* o = nsplit > 1 ? static_cast<float*>(ws_o_) + (gr * p.max_splits + s) * VD
+                                : static_cast<float*>(out_) + gr * VD;
+          o += 8 * si;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            *reinterpret_cast<f32x4*>(o + 64 * k) = x[2 * k] * inv;
+            *reinterpret_cast<f32x4*>(o + 64 * k + 4) = x[2 * k + 1] * inv;
           }
+        } else {
+          __bf16* o = static_cast<__bf16*>(out_) + gr * VD + 8 * si;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            *reinterpret_cast<bf16x8*>(o + 64 * k) = to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
         }
       }
     }
@@ -993,7 +1064,7 @@ hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st)
   const uint32_t* mw = p.mask_words;
   void* o = p.out;
   float* l = p.lse;
-  float* wo = p.ws_o;
+  void* wo = p.ws_o;
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
   void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mw, &o, &l, &wo, &wl, &sc};
