@@ -83,6 +83,16 @@ def test_plan_heuristic_fills_the_chip():
              total_mask=32 * 32800, num_slots=200000)
     pl = tv.plan(p)
     assert 200 <= pl["max_splits"] * pl["row_blocks"] <= 256
+    # a batch of unequal requests (32 x 1536 rows, the longest 65560 keys, 259k
+    # keys in all): splits near half a compute unit's share, so about two
+    # workgroups per compute unit once the longest-first order packs them
+    p = prob(batch=32, num_heads=64, total_q=768, max_q_len=24, max_kv_len=65560,
+             total_kv=259000, total_mask=24 * 259000, num_slots=262144)
+    pl = tv.plan(p)
+    share = -(-12 * -(-259000 // 32) // 512)
+    assert pl["split_keys"] == 32 * share
+    # the dispatch order costs one int32 per work item
+    assert tv.workspace_bytes(p) >= 32 * pl["max_splits"] * 12 * 4
 
 
 def test_bad_shapes_are_rejected():

@@ -43,6 +43,9 @@ struct Layout {
   int64_t words_off, words_bytes;
   int64_t wso_off, wso_bytes;
   int64_t wsl_off, wsl_bytes;
+  int64_t order_off, order_bytes;  // longest-first work order (0 bytes: natural order)
+  int32_t xcd_group;     // dispatch positions per XCD group
+  int64_t grid;          // split-kernel workgroups
   bool active;           // anything to compute
 };
 
@@ -75,14 +78,20 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   } else if (p->num_splits > 0) {
     split_keys = ceil_div(ceil_div(L, p->num_splits), tv::TILE_KEYS) * tv::TILE_KEYS;
   } else {
-    // one workgroup per compute unit over the whole batch, splits of >= 8 tiles
+    // splits of >= 8 tiles; one workgroup per compute unit over the whole
+    // request, or for a batch (requests of unequal lengths, dispatched longest
+    // first) about two, so that the schedule has pieces to balance with
     const int64_t kv_tiles = ceil_div(std::max<int64_t>(p->total_kv, L), tv::TILE_KEYS);
-    const int64_t per_wg = std::max<int64_t>(kMinSplitTiles, ceil_div(row_blocks * kv_tiles, kCUs));
+    const int64_t share = p->batch > 1 ? 2 * kCUs : kCUs;
+    const int64_t per_wg =
+        std::max<int64_t>(kMinSplitTiles, ceil_div(row_blocks * kv_tiles, share));
     split_keys = std::min<int64_t>(per_wg, ceil_div(L, tv::TILE_KEYS)) * tv::TILE_KEYS;
   }
   const int64_t max_splits = std::max<int64_t>(1, ceil_div(L, split_keys));
   const int64_t total_work = (int64_t)p->batch * max_splits * row_blocks;
-  if (total_work > kMaxInt32 - 8) return TV_ERR_SHAPE;
+  lay->xcd_group = (int32_t)std::min<int64_t>(row_blocks, 16);
+  if (total_work > kMaxInt32 - 8 * 16) return TV_ERR_SHAPE;
+  lay->grid = ceil_div(total_work, 8 * lay->xcd_group) * 8 * lay->xcd_group;
 
   lay->max_tiles = (int32_t)std::max<int64_t>(1, ceil_div(L, tv::TILE_KEYS));
   lay->words_off = 0;
@@ -99,6 +108,13 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
     lay->wsl_off = off;
     lay->wsl_bytes = align256(prow * (f16_parts ? 8 : 4));
     off += lay->wsl_bytes;
+  }
+  // requests of unequal lengths: a longest-first dispatch order (written by the
+  // pack kernel) balances the compute units
+  if (p->batch > 1 && L > 0 && total_work <= tv::SCHED_MAX_WORK) {
+    lay->order_off = off;
+    lay->order_bytes = align256(total_work * 4);
+    off += lay->order_bytes;
   }
   lay->plan.split_keys = (int32_t)split_keys;
   lay->plan.max_splits = (int32_t)max_splits;
@@ -145,9 +161,19 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     pp.qo_indptr = qo_indptr;
     pp.words = words;
     pp.max_tiles = lay.max_tiles;
-    const int64_t gx = ceil_div((int64_t)p->max_q_len * lay.max_tiles, 256);  // a word per thread
-    if (gx > kMaxInt32) return TV_ERR_SHAPE;
-    if (tv::launch_pack(pp, (int)gx, p->batch, s) != hipSuccess) return TV_ERR_LAUNCH;
+    pp.order = lay.order_bytes ? reinterpret_cast<int32_t*>(ws + lay.order_off) : nullptr;
+    pp.total_work = (int32_t)((int64_t)p->batch * lay.plan.max_splits * lay.plan.row_blocks);
+    pp.max_splits = lay.plan.max_splits;
+    pp.row_blocks = lay.plan.row_blocks;
+    pp.split_keys = lay.plan.split_keys;
+    pp.num_heads = p->num_heads;
+    pp.batch = p->batch;
+    // a wave per draft row and 512 keys (tv_pack_mask_kernel), 4 waves per workgroup
+    const int64_t gx = ceil_div((int64_t)p->max_q_len * ceil_div(p->max_kv_len, tv::PACK_KEYS), 4);
+    if (gx + 1 > kMaxInt32) return TV_ERR_SHAPE;
+    pp.sched_block = pp.order ? (int32_t)gx : -1;  // one more workgroup column
+    if (tv::launch_pack(pp, (int)gx + (pp.order ? 1 : 0), p->batch, s) != hipSuccess)
+      return TV_ERR_LAUNCH;
   }
 
   tv::SplitParams sp;
@@ -157,6 +183,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.kv_indptr = kv_indptr;
   sp.qo_indptr = qo_indptr;
   sp.mask_words = words;
+  sp.order = lay.order_bytes ? reinterpret_cast<const int32_t*>(ws + lay.order_off) : nullptr;
   sp.out = out;
   sp.lse = lse;
   sp.ws_o = lay.plan.merge ? static_cast<void*>(ws + lay.wso_off) : nullptr;
@@ -168,9 +195,10 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.s.row_blocks = lay.plan.row_blocks;
   sp.s.total_work = (int32_t)((int64_t)p->batch * lay.plan.max_splits * lay.plan.row_blocks);
   sp.s.max_tiles = lay.max_tiles;
+  sp.s.xcd_group = lay.xcd_group;
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
   sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
-  const int grid = (int)ceil_div(sp.s.total_work, 8) * 8;
+  const int grid = (int)lay.grid;
   if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return TV_ERR_LAUNCH;
   if (tv::launch_split(sp, grid, p->out_dtype, s) != hipSuccess) return TV_ERR_LAUNCH;
   if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return TV_ERR_LAUNCH;

@@ -18,8 +18,14 @@ constexpr int QK = 576;           // key / query dims (512 latent + 64 RoPE)
 constexpr int VD = 512;           // value dims
 constexpr int ROWS_PER_WG = 128;  // query rows (draft x head) per workgroup: 4 waves x 32
 constexpr int TILE_KEYS = 32;     // keys per LDS tile
+constexpr int PACK_KEYS = 512;    // keys of a draft row one wave of tv_pack_mask_kernel packs
 constexpr int OUT_BF16 = 0;
 constexpr int OUT_F32 = 1;
+
+// Work item w of the split kernel: request b, KV split s, row block rb with
+// w = (b * max_splits + s) * row_blocks + rb.
+constexpr int SCHED_BUCKETS = 1024;  // split-length classes of the longest-first order
+constexpr int SCHED_MAX_WORK = 65536;  // larger grids keep the natural order
 
 struct PackParams {
   const uint8_t* mask;
@@ -28,6 +34,9 @@ struct PackParams {
   const int32_t* qo_indptr;
   uint32_t* words;            // [total_q, max_tiles] visibility words
   int32_t max_tiles;          // ceil(max_kv_len / 32)
+  int32_t sched_block;        // blockIdx.x of the workgroup that writes `order` (-1: none)
+  int32_t* order;             // [total_work]: work item at dispatch position p, or -1
+  int32_t total_work, max_splits, row_blocks, split_keys, num_heads, batch;
 };
 
 struct SplitScalars {
@@ -38,6 +47,7 @@ struct SplitScalars {
   int32_t row_blocks;
   int32_t total_work;         // batch * max_splits * row_blocks
   int32_t max_tiles;
+  int32_t xcd_group;          // dispatch positions per XCD group (see tv_split_kernel)
 };
 
 struct SplitParams {
@@ -47,6 +57,7 @@ struct SplitParams {
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;
   const uint32_t* mask_words; // [total_q, max_tiles] from tv_pack_mask_kernel
+  const int32_t* order;       // longest-first work order from tv_pack_mask_kernel, or null
   void* out;                  // [total_q, H, 512] bf16 or fp32 (requests with one split)
   float* lse;                 // [total_q, H]
   // partial outputs [total_q * H, max_splits, 512]: fp32 in precise mode, else

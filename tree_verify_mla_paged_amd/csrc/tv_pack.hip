@@ -14,28 +14,94 @@
 namespace tv {
 
 // Word (token qo_indptr[b] + i, tile) bit k = mask byte of key 32*tile + k of draft i;
-// keys at or past L_b give 0.  One word per thread: consecutive threads take
-// consecutive tiles of a draft row, so a wave reads 64 consecutive 32-byte
-// runs, all 32 byte loads of a thread in flight at once.
+// keys at or past L_b give 0.  One wave per PACK_SEGS * 64 keys of a draft row:
+// lane l reads key 64j + l of each 64-key segment j (one coalesced 64-byte load
+// per segment), and the segment's ballot is its two words; lanes 0..2*PACK_SEGS-1
+// then store one word each.
+constexpr int PACK_SEGS = PACK_KEYS / 64;
+
+// Longest-first dispatch order of the split kernel's work items, by one
+// workgroup: the splits (b, s) that exist are bucketed by their key count
+// (SCHED_BUCKETS classes, longest first; a counting sort), and each takes as many
+// consecutive positions as its request has row blocks, one per row block, so
+// the row blocks of a split stay together.  Positions left over hold -1.  With
+// the hardware dispatching workgroups in position order as compute units free
+// up, this is greedy longest-processing-time scheduling.
+__device__ void schedule_work(const PackParams& p) {
+  __shared__ int cnt[SCHED_BUCKETS];
+  const int t = threadIdx.x;
+  for (int i = t; i < p.total_work; i += 256) p.order[i] = -1;
+  for (int i = t; i < SCHED_BUCKETS; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const int units = p.batch * p.max_splits;
+  // bucket of a split and the row blocks it holds (0: the split does not exist)
+  auto classify = [&](int u, int& bucket) -> int {
+    const int b = u / p.max_splits, s = u - b * p.max_splits;
+    const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
+    const int nsplit = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
+    if (s >= nsplit) return 0;
+    const int keys = L > 0 ? min(L - s * p.split_keys, p.split_keys) : 0;
+    bucket = (int)((int64_t)(p.split_keys - keys) * (SCHED_BUCKETS - 1) / p.split_keys);
+    const int rows = (p.qo_indptr[b + 1] - p.qo_indptr[b]) * p.num_heads;
+    return (rows + ROWS_PER_WG - 1) / ROWS_PER_WG;
+  };
+  for (int u = t; u < units; u += 256) {
+    int bucket;
+    const int rbs = classify(u, bucket);
+    if (rbs > 0) atomicAdd(&cnt[bucket], rbs);
+  }
+  __syncthreads();
+  if (t == 0) {  // exclusive prefix sum, longest class first
+    int run = 0;
+    for (int i = 0; i < SCHED_BUCKETS; ++i) {
+      const int c = cnt[i];
+      cnt[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int u = t; u < units; u += 256) {
+    int bucket;
+    const int rbs = classify(u, bucket);
+    if (rbs == 0) continue;
+    const int start = atomicAdd(&cnt[bucket], rbs);
+    for (int rb = 0; rb < rbs; ++rb) p.order[start + rb] = u * p.row_blocks + rb;
+  }
+}
+
 __global__ __launch_bounds__(256) void tv_pack_mask_kernel(PackParams p) {
+  if ((int)blockIdx.x == p.sched_block) {
+    if (blockIdx.y == 0) schedule_work(p);
+    return;
+  }
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
   const int n = p.qo_indptr[b + 1] - q0;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
   const int tiles = (L + TILE_KEYS - 1) / TILE_KEYS;
-  const int w = blockIdx.x * 256 + threadIdx.x;
-  if (w >= n * tiles) return;
-  const int i = w / tiles;
-  const int tile = w - i * tiles;
-  const int nk = min(TILE_KEYS, L - tile * TILE_KEYS);
-  const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * L + tile * TILE_KEYS;
-  uint8_t v[TILE_KEYS];
+  const int chunks = (L + 64 * PACK_SEGS - 1) / (64 * PACK_SEGS);
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // wave-uniform
+  if (unit >= n * chunks) return;
+  const int i = unit / chunks;
+  const int c = unit - i * chunks;
+  const int lane = threadIdx.x & 63;
+  const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * L;
+  const int k0 = c * 64 * PACK_SEGS + lane;
+  uint8_t v[PACK_SEGS];
 #pragma unroll
-  for (int k = 0; k < TILE_KEYS; ++k) v[k] = k < nk ? m[k] : 0;
-  uint32_t word = 0;
+  for (int j = 0; j < PACK_SEGS; ++j) {
+    const int k = k0 + 64 * j;
+    v[j] = k < L ? m[k] : 0;
+  }
+  uint32_t mine = 0;
 #pragma unroll
-  for (int k = 0; k < TILE_KEYS; ++k) word |= (v[k] != 0 ? 1u : 0u) << k;
-  p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = word;
+  for (int j = 0; j < PACK_SEGS; ++j) {
+    const unsigned long long bal = __ballot(v[j] != 0);
+    if (lane == 2 * j) mine = (uint32_t)bal;
+    if (lane == 2 * j + 1) mine = (uint32_t)(bal >> 32);
+  }
+  const int tile = c * 2 * PACK_SEGS + lane;
+  if (lane < 2 * PACK_SEGS && tile < tiles) p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = mine;
 }
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st) {

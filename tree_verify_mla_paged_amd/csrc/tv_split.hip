@@ -576,24 +576,30 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, con
                                         f32x16 (&O)[16], bool resc, const float* alpha_t,
                                         const bf16x8 (&A0)[2], Bg&& bg) {
   if (resc) {
-    // some row's reference moved: scale this wave's O slice of every row
-    // (accumulator O[4*db + rb] holds rows 32*rb + lane % 32)
+    // some row's reference moved: scale this wave's O slice of the rows, for
+    // each 32-row block that holds such a row (accumulator O[4*db + rb] holds
+    // rows 32*rb + lane % 32; the branch per block is uniform)
     float a4[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) a4[rb] = alpha_t[32 * rb + (c.lane & 31)];
-    // element by element, in place in the AGPRs: O must never have a
-    // definition outside the accumulator register class in the loop
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int rb = 0; rb < 4; ++rb) {
+      if (__any(a4[rb] != 1.f)) {
+        // element by element, in place in the AGPRs: O must never have a
+        // definition outside the accumulator register class in the loop
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float tmp;
-        asm volatile(
-            "v_accvgpr_read_b32 %1, %0\n\t"
-            "v_mul_f32 %1, %1, %2\n\t"
-            "v_accvgpr_write_b32 %0, %1"
-            : "+a"(O[i][r]), "=&v"(tmp)
-            : "v"(a4[i & 3]));
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(O[4 * db + rb][r]), "=&v"(tmp)
+                : "v"(a4[rb]));
+          }
+        }
       }
     }
     asm volatile("s_nop 3");  // accumulator writes before the next MFMA reads them
@@ -842,8 +848,8 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
     const int32_t* __restrict__ qo_indptr_, const uint32_t* __restrict__ mask_words_,
-    void* __restrict__ out_, float* __restrict__ lse_, void* __restrict__ ws_o_,
-    float* __restrict__ ws_lse_, SplitScalars p) {
+    const int32_t* __restrict__ order_, void* __restrict__ out_, float* __restrict__ lse_,
+    void* __restrict__ ws_o_, float* __restrict__ ws_lse_, SplitScalars p) {
   __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[2 * (PRECISE ? 2 * PBUF_LO : PBUF_LO)];
   __shared__ float inv_s[ROWS_PER_WG];
@@ -858,11 +864,18 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // blockIdx -> work item: consecutive work items (the row blocks of one KV
-  // split) go to the same XCD, which dispatch fills round-robin by blockIdx.
-  const int per_xcd = gridDim.x / 8;
-  const int work = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (work >= p.total_work) return;
+  // blockIdx -> dispatch position -> work item.  Dispatch fills the 8 XCDs
+  // round-robin by blockIdx; XCD x = blockIdx % 8 takes groups of xcd_group
+  // consecutive positions (the row blocks of a KV split share its gathered
+  // tiles through that XCD's L2), the groups going round-robin over the XCDs
+  // in position order (gridDim.x is a multiple of 8 * xcd_group).  Positions
+  // map to work items through the longest-first order when there is one.
+  const int G = p.xcd_group;
+  const int xk = blockIdx.x >> 3;
+  const int pos = (((xk / G) << 3) + (blockIdx.x & 7)) * G + xk % G;
+  if (pos >= p.total_work) return;
+  const int work = order_ ? order_[pos] : pos;
+  if (work < 0) return;
   const int rb = work % p.row_blocks;
   const int s = (work / p.row_blocks) % p.max_splits;
   const int b = work / (p.row_blocks * p.max_splits);
@@ -1062,12 +1075,13 @@ hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st)
   const int32_t* kvp = p.kv_indptr;
   const int32_t* qop = p.qo_indptr;
   const uint32_t* mw = p.mask_words;
+  const int32_t* ord = p.order;
   void* o = p.out;
   float* l = p.lse;
   void* wo = p.ws_o;
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
-  void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mw, &o, &l, &wo, &wl, &sc};
+  void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mw, &ord, &o, &l, &wo, &wl, &sc};
   // [out dtype][wide][precise]
   static const void* const fns[2][2][2] = {
       {{reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false, false>),
