@@ -15,13 +15,14 @@
 
 namespace tv {
 
-// One row per workgroup, in chunks of up to MERGE_CHUNK splits.  The chunk's
-// split LSEs are read once, cooperatively, and turned into weights in LDS;
-// then every partial-output load is issued with its weight already known (no
-// load waits on another), U per thread in flight.  Thread t owns value dims
-// 4*(t & 127) .. +3; the two halves of the workgroup take alternate splits and
-// combine through LDS.  Weights are relative to the running maximum M and are
-// rescaled when a later chunk raises it.
+// One row per workgroup, in chunks of up to MERGE_CHUNK splits.  A thread's
+// first U partial-output loads go out before anything else; meanwhile the
+// chunk's split LSEs are read once, cooperatively, and turned into weights in
+// LDS.  Each load is 16 bytes: a
+// thread owns DPT value dims (8 fp16 or 4 fp32), so a split's row takes TPS
+// threads and the workgroup's NPH = 256 / TPS phases take alternate splits,
+// combined through LDS at the end.  Weights are relative to the running
+// maximum M and are rescaled when a later chunk raises it.
 constexpr int MERGE_CHUNK = 1024;
 
 // Maximum over the workgroup (256 threads); ends with a barrier.
@@ -37,11 +38,15 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 template <int OUT, bool F16P>
 __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
-  constexpr int U = 16;
+  constexpr int U = 16;               // loads per thread in flight
+  constexpr int DPT = F16P ? 8 : 4;  // value dims per thread: one 16-byte load
+  constexpr int TPS = VD / DPT;      // threads per split row
+  constexpr int NPH = 256 / TPS;     // splits in flight across the workgroup
+  typedef float accv __attribute__((ext_vector_type(DPT)));
   __shared__ float wgt_s[MERGE_CHUNK];               // w_s
   __shared__ float wnum_s[F16P ? MERGE_CHUNK : 1];   // w_s 2^k_s
-  __shared__ f32x4 part_o[128];
-  __shared__ float part_w[128];
+  __shared__ accv part_o[NPH - 1][TPS];
+  __shared__ float part_w[NPH - 1][TPS];
   __shared__ float red[4];
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
@@ -55,21 +60,35 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
   const int LS = F16P ? 2 : 1;  // floats per (row, split) in ws_lse
   const float* ls = p.ws_lse + g * p.max_splits * LS;
   const int t = threadIdx.x;
-  const int d = (t & 127) * 4;
-  const int h = t >> 7;
+  const int d = (t % TPS) * DPT;
+  const int h = t / TPS;  // phase: splits h, h + NPH, ...
   const float* po = static_cast<const float*>(p.ws_o) + g * p.max_splits * VD + d;
   const _Float16* ph = static_cast<const _Float16*>(p.ws_o) + g * p.max_splits * VD + d;
 
   float M = -INFINITY;  // running maximum of the split LSEs
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  accv acc = accv{};
   float W = 0.f;  // this thread's share of sum_s exp(lse_s - M)
+  f32x4 v[U];
+  f16x8 vh[U];
+  // the partial outputs of splits c0 + s0 + NPH*j: every split below ns was
+  // written by the split kernel (an empty one as zeros), so these loads need
+  // no weight and go out before the weights are known
+  auto load_batch = [&](int c0, int s0) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int s = c0 + s0 + NPH * j;
+      if (F16P) vh[j] = s < ns ? *reinterpret_cast<const f16x8*>(ph + (int64_t)s * VD) : f16x8{};
+      else v[j] = s < ns ? *reinterpret_cast<const f32x4*>(po + (int64_t)s * VD) : f32x4{};
+    }
+  };
   for (int c0 = 0; c0 < ns; c0 += MERGE_CHUNK) {
     const int nc = min(MERGE_CHUNK, ns - c0);
+    load_batch(c0, h);
     float m = -INFINITY;
     for (int i = t; i < nc; i += 256) {
-      const float v = ls[LS * (c0 + i)];
-      wgt_s[i] = v;
-      m = fmaxf(m, v);
+      const float lv = ls[LS * (c0 + i)];
+      wgt_s[i] = lv;
+      m = fmaxf(m, lv);
     }
     const float Mn = fmaxf(M, block_max(m, red));
     if (Mn == -INFINITY) continue;  // every split so far is empty (uniform)
@@ -86,56 +105,52 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
       if (F16P) wnum_s[i] = __builtin_ldexpf(w, (int)ls[LS * (c0 + i) + 1]);
     }
     __syncthreads();
-    for (int s0 = h; s0 < nc; s0 += 2 * U) {
-      f32x4 v[U];
-      f16x4 vh[U];
-      float wv[U], wn[U];
+    for (int s0 = h; s0 < nc; s0 += NPH * U) {
+      if (s0 != h) load_batch(c0, s0);
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int s = s0 + 2 * j;
-        wv[j] = s < nc ? wgt_s[s] : 0.f;
-        if (F16P) {
-          wn[j] = s < nc ? wnum_s[s] : 0.f;
-          vh[j] = wv[j] > 0.f ? *reinterpret_cast<const f16x4*>(ph + (int64_t)(c0 + s) * VD)
-                              : f16x4{};
-        } else {
-          v[j] = wv[j] > 0.f ? *reinterpret_cast<const f32x4*>(po + (int64_t)(c0 + s) * VD)
-                             : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
+        const int s = s0 + NPH * j;
+        const float wv = s < nc ? wgt_s[s] : 0.f;
+        if constexpr (F16P) {
+          const float wn = s < nc ? wnum_s[s] : 0.f;
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (F16P) {
-          acc += wn[j] * f32x4{(float)vh[j][0], (float)vh[j][1], (float)vh[j][2],
-                               (float)vh[j][3]};
+          for (int e = 0; e < DPT; ++e) acc[e] += wn * (float)vh[j][e];
         } else {
-          acc += wv[j] * v[j];
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) acc[e] += wv * v[j][e];
         }
-        W += wv[j];
+        W += wv;
       }
     }
     __syncthreads();  // wgt_s is rewritten by the next chunk
   }
-  if (h == 1) {
-    part_o[t & 127] = acc;
-    part_w[t & 127] = W;
+  if (h > 0) {
+    part_o[h - 1][t % TPS] = acc;
+    part_w[h - 1][t % TPS] = W;
   }
   __syncthreads();
-  if (h == 1) return;
-  acc += part_o[t];
-  W += part_w[t];
+  if (h > 0) return;
+#pragma unroll
+  for (int k = 0; k < NPH - 1; ++k) {
+    acc += part_o[k][t];
+    W += part_w[k][t];
+  }
   if (M != -INFINITY) acc *= 1.f / W;
   const float lse = (M == -INFINITY) ? -INFINITY : M + logf(W);
   if (t == 0) p.lse[g] = lse;
-  if (OUT == OUT_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + g * VD + d) = acc;
-  } else {
-    bf16x4 o;
-    o[0] = (__bf16)acc[0];
-    o[1] = (__bf16)acc[1];
-    o[2] = (__bf16)acc[2];
-    o[3] = (__bf16)acc[3];
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + g * VD + d) = o;
+#pragma unroll
+  for (int e0 = 0; e0 < DPT; e0 += 4) {
+    const f32x4 o4 = f32x4{acc[e0], acc[e0 + 1], acc[e0 + 2], acc[e0 + 3]};
+    if (OUT == OUT_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + g * VD + d + e0) = o4;
+    } else {
+      bf16x4 o;
+      o[0] = (__bf16)o4[0];
+      o[1] = (__bf16)o4[1];
+      o[2] = (__bf16)o4[2];
+      o[3] = (__bf16)o4[3];
+      *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.out) + g * VD + d + e0) = o;
+    }
   }
 }
 
