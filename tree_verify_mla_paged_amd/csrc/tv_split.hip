@@ -850,13 +850,15 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const int32_t* __restrict__ qo_indptr_, const uint32_t* __restrict__ mask_words_,
     const int32_t* __restrict__ order_, void* __restrict__ out_, float* __restrict__ lse_,
     void* __restrict__ ws_o_, float* __restrict__ ws_lse_, SplitScalars p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stages_s[NSTAGE * STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t pbuf_s[2 * (PRECISE ? 2 * PBUF_LO : PBUF_LO)];
+  // one LDS block: the tile stages, then the two P buffers (the epilogue's two
+  // staging buffers span both), then the slot rings
+  constexpr int PB2 = 2 * (PRECISE ? 2 * PBUF_LO : PBUF_LO);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_s[NSTAGE * STAGE + PB2 + 4 * SLOT_RING * 256];
   __shared__ float inv_s[ROWS_PER_WG];
-  __shared__ __attribute__((aligned(1024))) uint8_t sring_s[4 * SLOT_RING * 256];
   __shared__ float alpha_s[2 * ROWS_PER_WG];
-  lds_u8* const stages = (lds_u8*)stages_s;
-  lds_u8* const pbuf = (lds_u8*)pbuf_s;
+  lds_u8* const stages = (lds_u8*)lds_s;
+  lds_u8* const pbuf = stages + NSTAGE * STAGE;
+  lds_u8* const sring_s = pbuf + PB2;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   c.wave = wave;
   c.lane = lane;
   c.scale_log2 = p.scale_log2;
-  c.sring = (lds_u8*)sring_s + wave * (SLOT_RING * 256);
+  c.sring = sring_s + wave * (SLOT_RING * 256);
 
   const int i0 = row0 / H;
   const int nd = (min(row0 + ROWS_PER_WG, R) - 1) / H - i0 + 1;
@@ -989,24 +991,21 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   // O^T -> LDS -> global, one row block (32 rows) at a time: wave w puts its
   // 128 dims of the 32 rows into region w ([32 rows][EP_ROW bytes]); then 8
   // lanes store each row: lane i of a row covers dims 64k + 8i .. +7, k = 0..7,
-  // so that each store instruction writes whole contiguous row segments.  The
-  // row-block loop is rolled (this code runs once per workgroup).
+  // so that each store instruction writes whole contiguous row segments.  Two
+  // staging buffers: the row block after the current one is staged while the
+  // current one's stores drain.  The row-block loop is rolled (this code runs
+  // once per workgroup).
   constexpr int EP_ROW = 528;  // 512 bytes of a row's 128 dims, + 16: conflict-free writes
-  static_assert(4 * 32 * EP_ROW <= NSTAGE * STAGE, "");
+  constexpr int EPB = 4 * 32 * EP_ROW;
+  static_assert(2 * EPB <= NSTAGE * STAGE + PB2, "");
   {
     lds_u8* ep = stages + wave * 32 * EP_ROW + l32 * EP_ROW + 16 * half;
     const int lr = tid >> 3, si = tid & 7;       // row within the row block, lane in the row
-    const lds_u8* rd = stages + lr * EP_ROW + 32 * si;  // dims 8*si of chunk k = 0
+    stage_rows<0>(ep, O);
+    __syncthreads();
 #pragma unroll 1
     for (int rb = 0; rb < 4; ++rb) {
-      if (rb > 0) __syncthreads();  // the previous row block has been read back
-      switch (rb) {
-        case 0: stage_rows<0>(ep, O); break;
-        case 1: stage_rows<1>(ep, O); break;
-        case 2: stage_rows<2>(ep, O); break;
-        default: stage_rows<3>(ep, O); break;
-      }
-      __syncthreads();
+      const lds_u8* rd = stages + (rb & 1) * EPB + lr * EP_ROW + 32 * si;  // chunk k = 0
       const int rl = 32 * rb + lr;  // row within the workgroup's block
       // chunk k: dims 64k + 8*si: region k/2, byte offset 256*(k&1) + 32*si
       f32x4 x[16];
@@ -1061,6 +1060,14 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
             *reinterpret_cast<bf16x8*>(o + 64 * k) = to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
         }
       }
+      // the next row block into the other buffer (last read two blocks ago)
+      switch (rb) {
+        case 0: stage_rows<1>(ep + EPB, O); break;
+        case 1: stage_rows<2>(ep, O); break;
+        case 2: stage_rows<3>(ep + EPB, O); break;
+        default: break;
+      }
+      __syncthreads();
     }
   }
 }
