@@ -32,7 +32,7 @@ namespace {
 
 constexpr int64_t kMaxInt32 = 2147483647;
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kMinSplitTiles = 8;  // keys per split >= 256 unless the caller asks otherwise
+constexpr int kMinSplitTiles = 4;  // keys per split >= 128 unless the caller asks otherwise
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -78,7 +78,7 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   } else if (p->num_splits > 0) {
     split_keys = ceil_div(ceil_div(L, p->num_splits), tv::TILE_KEYS) * tv::TILE_KEYS;
   } else {
-    // splits of >= 8 tiles; one workgroup per compute unit over the whole
+    // splits of >= 4 tiles; one workgroup per compute unit over the whole
     // request, or for a batch (requests of unequal lengths, dispatched longest
     // first) about two, so that the schedule has pieces to balance with
     const int64_t kv_tiles = ceil_div(std::max<int64_t>(p->total_kv, L), tv::TILE_KEYS);
