@@ -273,6 +273,36 @@ def test_score_jumps_beyond_headroom_rescale(flags):
         full_check(w, num_splits=ns, out_f32=True, label="jump ns=%d" % ns, flags=flags)
 
 
+@pytest.mark.parametrize("e", [20, -20])
+def test_fp16_partials_keep_value_scale(e):
+    """Split partial outputs are fp16 under a power-of-two scale per (row,
+    split).  K/V scaled by 2^e and Q by 2^-e leave every score unchanged and
+    scale the output by exactly 2^e: at 2^20 unscaled fp16 partials would
+    overflow, at 2^-20 they would underflow.  Compared at the normal bar after
+    undoing the scale."""
+    w = W.small(250, [900], [6], num_heads=8)
+    w.q[:] = W.bf16_round(W.bf16_to_f32(w.q) * np.float32(2.0 ** -e))
+    ref = w.kv_indices
+    w.kv[ref] = W.bf16_round(W.bf16_to_f32(w.kv[ref]) * np.float32(2.0 ** e))
+    ro, rl = oracle.run(w)
+    for ns in (0, 5):
+        print("fp16 partial scale e=%d ns=%d" % (e, ns), flush=True)
+        o, l = run(w, num_splits=ns, out_f32=True)
+        compare(np.asarray(o, np.float64) * 2.0 ** -e, l, ro * 2.0 ** -e, rl, bf16_out=False,
+                label="scale 2^%d ns=%d" % (e, ns),
+                extra_abs=p_rounding_bound(w, precise=False) * 2.0 ** -e)
+
+
+@pytest.mark.parametrize("ns", [0, 5])
+def test_batch_longest_first_order(ns):
+    """A batch of very unequal requests with several row blocks each (288 rows
+    at 48 heads): the longest-first dispatch order must cover every (request,
+    split, row block) exactly once."""
+    print("longest-first batch ns=%d" % ns, flush=True)
+    w = W.small(251, [3000, 10, 700, 0, 1500, 64, 2500], [5, 3, 6, 2, 4, 1, 6], num_heads=48)
+    full_check(w, num_splits=ns, label="lpt ns=%d" % ns)
+
+
 # ------------------------------------------------------------ capture
 
 def test_hip_graph_capture_and_replay():
