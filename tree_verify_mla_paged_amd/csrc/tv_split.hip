@@ -944,15 +944,19 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   if (c.ntiles > 0) split_start<WIDE>(stages, c);
 
   // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7), all 576
-  // dims in VGPRs for the whole split.  A row past the request's rows uses the
-  // block's first row instead: its scores stay in its own lane, are masked
-  // off, and it writes nothing.
+  // dims in VGPRs for the whole split.  A row past the request's rows loads
+  // nothing (zeros): its scores stay in its own lane, are masked off, and it
+  // writes nothing.
   bf16x8 qf[QK / 16];
   {
     const int64_t gq = c.row_ok ? g : (int64_t)q0 * H + row0;
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_ + gq * QK + half * 8);
 #pragma unroll
-    for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = qp[2 * ks];
+    for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = bf16x8{};
+    if (c.row_ok) {
+#pragma unroll
+      for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = qp[2 * ks];
+    }
   }
   // every Q load has landed before the tile loop (an asm use of each register
   // makes the compiler wait here): otherwise it keeps the qf registers pending
@@ -1001,10 +1005,11 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   {
     lds_u8* ep = stages + wave * 32 * EP_ROW + l32 * EP_ROW + 16 * half;
     const int lr = tid >> 3, si = tid & 7;       // row within the row block, lane in the row
+    const int nrb = min(4, (R - row0 + 31) >> 5);  // row blocks holding a row of the request
     stage_rows<0>(ep, O);
     __syncthreads();
 #pragma unroll 1
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < nrb; ++rb) {
       const lds_u8* rd = stages + (rb & 1) * EPB + lr * EP_ROW + 32 * si;  // chunk k = 0
       const int rl = 32 * rb + lr;  // row within the workgroup's block
       // chunk k: dims 64k + 8*si: region k/2, byte offset 256*(k&1) + 32*si
@@ -1061,7 +1066,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
         }
       }
       // the next row block into the other buffer (last read two blocks ago)
-      switch (rb) {
+      switch (rb + 1 < nrb ? rb : 3) {
         case 0: stage_rows<1>(ep + EPB, O); break;
         case 1: stage_rows<2>(ep, O); break;
         case 2: stage_rows<3>(ep + EPB, O); break;
