@@ -11,8 +11,9 @@
 //
 // Method: KV-split flash decoding with an LSE merge (page 2, section "The
 // Broader Context").  One workgroup per (request, 128-row block, KV split);
-// with more than one split it writes a normalised partial output and its LSE,
-// which tv_merge_kernel combines.
+// with more than one split it writes a partial output (fp16 under a power-of-
+// two scale, or fp32 in precise mode) and its LSE, which tv_merge_kernel
+// combines.
 //
 // gfx950 mapping
 //  * 4 wave64s; wave w owns 32 query rows (rows of a request are (draft, head)
@@ -22,33 +23,37 @@
 //    per wave moves the 64 RoPE dims of 8 keys, one moves the visibility words.
 //    No registers hold in-flight tile data; three LDS stages keep two tiles in
 //    flight.  The gathers are inline asm tracked with explicit vmcnt waits, so
-//    the compiler sees no aliasing between them and the LDS reads, and the tile
-//    loop is one body with a run-time stage.
+//    the compiler sees no aliasing between them and the LDS reads.
 //  * S^T[key, row] = K[key, :] . Q[row, :] with v_mfma_f32_32x32x16_bf16:
 //    A = key rows read from LDS (ds_read_b128), B = the wave's query rows held
 //    in VGPRs for the whole split.  In the 32x32 accumulator layout lane l holds
-//    row l % 32 and 16 of the 32 keys: the row max / sum is a 16-register
-//    reduction plus one exchange with lane l ^ 32.
+//    row l % 32 and 16 of the 32 keys: the row max is a 16-register reduction
+//    plus one exchange with lane l ^ 32 (v_permlane32_swap).
 //  * O^T[d, row] += V^T[d, key] . P^T[key, row] is split by value dims instead:
 //    wave w owns dims 128w..128w+127 of all 128 rows (16 accumulators, the 256
 //    AGPRs), so the V tile is read once per workgroup rather than once per
-//    wave.  The bf16 probabilities go through a small LDS buffer in exactly the
+//    wave.  The bf16 probabilities go through an LDS buffer in exactly the
 //    MFMA B operand layout; A = V^T read straight from the row-major tile with
 //    ds_read_b64_tr_b16 (within 16 lanes, output lane i element j comes from
 //    source lane 4j + i/4, element i%4: when source lane 4j+q points at dims
 //    d0+4q.. of key j, lane i gets keys j=0..3 at dim d0+i).
+//  * Software pipeline, one barrier per tile (run_split): the QK chain of tile
+//    t+1 carries the gathers of tile t+2 in its shadow, the PV of tile t carries
+//    the softmax of tile t+1, a few fenced instructions after each MFMA (one
+//    wave per SIMD issues about one instruction every four cycles, so only a
+//    handful fit beside each MFMA for free).
 //  * Reference maximum with thresholded rescaling: a row's reference is set at
 //    the maximum of its first tile with a visible key (O and l are still
 //    exactly 0 then) and moves only when a score exceeds it by more than TAU
 //    (log2 units).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32
 //    sums and bf16 operands hold, so in the common case no VALU work touches
 //    the accumulators.  When a row's reference moves, its l and O are scaled by
-//    2^(old - new); the factor goes through LDS because every wave holds a
-//    slice of every row's O, and the whole workgroup takes that branch after
-//    the barrier that publishes P.
-//  * The kernel's straight-line code runs cold once per workgroup (instruction
-//    fetch), so prologue, loop and epilogue are kept compact: accumulators are
-//    zeroed by MFMAs, the epilogue is a rolled loop over LDS-staged rows.
+//    2^(old - new): the factors go through LDS (every wave holds a slice of
+//    every row's O), and each wave rescales, in place in the AGPRs, only the
+//    32-row blocks that hold a moved row.
+//  * Prologue and epilogue run once per workgroup: accumulators are zeroed by
+//    MFMAs; the epilogue stages O through LDS in two buffers and stores rows
+//    as contiguous runs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
