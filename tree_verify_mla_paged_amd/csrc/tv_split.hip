@@ -668,16 +668,22 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, con
   }
 }
 
-// Start of the split (c.ntiles >= 1; nothing outstanding): the slots of tiles
-// 0 and 1 (waited for here) and 2, then the gathers of tiles 0 and 1.
-template <bool WIDE>
-__device__ __forceinline__ void split_start(lds_u8* stages, const SplitCtx& c) {
-  int slot[8];
-  SlotRaw r;
+// Start of the split (c.ntiles >= 1), in two parts around the query loads.
+// split_slots: the slot loads of tiles 0..2 (nothing outstanding before them).
+__device__ __forceinline__ void split_slots(const SplitCtx& c) {
   slot_dma(c, 0);
   slot_dma(c, 1);
   slot_dma(c, 2);
-  wait_vmcnt<0>();
+}
+// split_gathers: once the slots have landed, the gathers of tiles 0 and 1.  QN
+// is the number of vector loads issued since split_slots (the wave's query
+// loads): waiting until at most QN are outstanding covers the three slot loads
+// and leaves the query rows in flight.
+template <bool WIDE, int QN>
+__device__ __forceinline__ void split_gathers(lds_u8* stages, const SplitCtx& c) {
+  int slot[8];
+  SlotRaw r;
+  wait_vmcnt<QN>();
   slot_load(r, c, 0);
   slot_take(slot, r, 0);
   slot_take(slot, r, 1);
@@ -741,7 +747,7 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
   return qk_tile_bg(stages + nx1 * STAGE, qf, c, bg);
 }
 
-// All tiles of the split after split_start, software-pipelined, one barrier per
+// All tiles of the split after split_gathers, software-pipelined, one barrier per
 // tile.  Tile k sits in stage k % 3, its P in P buffer k % 2 and its rescale
 // factors in alpha_s[k % 2].  Iteration t, after its barrier, runs the QK chain
 // of tile t+1 (qk_phase: the gathers of tile t+2 in its shadow), then the PV of
@@ -753,18 +759,25 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
 // tile 0 runs ahead of the loop.
 template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds_u8* pbuf,
-                                          const bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
+                                          bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
                                           float& m_ref, float& l_sum, float* alpha_s) {
   constexpr int PB = PRECISE ? 2 * PBUF_LO : PBUF_LO;  // bytes of one P buffer
   const int nt = c.ntiles;
   const uint32_t alpha_lds = lds_addr((lds_u8*)alpha_s);
-  // tile 0: its gathers landed (only tile 1's may be outstanding), QK, softmax
+  // tile 0: its gathers landed, and with them the query loads issued before
+  // them (only tile 1's gathers may be outstanding); QK, softmax
   if (nt > 1) wait_vmcnt<DMA_PER_TILE>();
   else wait_vmcnt<0>();
   __syncthreads();
   Soft sm;
   {
     f32x16 S = qk_tile(stages, qf, c);
+    // every query register is known to have landed before the tile loop (an
+    // asm use of each makes the compiler wait here at the latest): otherwise
+    // it keeps them pending at the loop header and puts a vmcnt wait before
+    // each QK MFMA, which in steady state waits out the tile gathers instead
+#pragma unroll
+    for (int ks = 0; ks < QK / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
     const uint32_t mw = tile_mask(stages, c, 0);
 #pragma unroll
     for (int st = 0; st < SOFT_STEPS; ++st)
@@ -944,31 +957,28 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   }
   c.mw_off = MAIN_BYTES + ROPE_BYTES + 4 * dl;
 
-  // the first two tiles' gathers go out before the query rows are loaded, so
-  // their memory latency overlaps the loads below
-  if (c.ntiles > 0) split_start<WIDE>(stages, c);
+  // prologue: the slot loads, then the query rows (their transfer overlaps the
+  // slots' round trip), then the first two tiles' gathers
+  if (c.ntiles > 0) split_slots(c);
 
   // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7), all 576
   // dims in VGPRs for the whole split.  A row past the request's rows loads
   // nothing (zeros): its scores stay in its own lane, are masked off, and it
-  // writes nothing.
+  // writes nothing.  A wave issues the QK / 16 loads iff it has a row of the
+  // request (uniform: its first row is one).
   bf16x8 qf[QK / 16];
-  {
-    const int64_t gq = c.row_ok ? g : (int64_t)q0 * H + row0;
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_ + gq * QK + half * 8);
+  const bool wave_q = row0 + wave * 32 < R;
 #pragma unroll
-    for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = bf16x8{};
+  for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = bf16x8{};
+  if (c.ntiles > 0) {
     if (c.row_ok) {
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_ + g * QK + half * 8);
 #pragma unroll
       for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = qp[2 * ks];
     }
+    if (wave_q) split_gathers<WIDE, QK / 16>(stages, c);
+    else split_gathers<WIDE, 0>(stages, c);
   }
-  // every Q load has landed before the tile loop (an asm use of each register
-  // makes the compiler wait here): otherwise it keeps the qf registers pending
-  // at the loop header and puts a vmcnt wait before each QK MFMA, which in
-  // steady state waits out the tile gathers instead
-#pragma unroll
-  for (int ks = 0; ks < QK / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
   // 4*(l/32) + r%4) and rows 32*rb + l%32: accumulator O[4*db + rb]
