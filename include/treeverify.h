@@ -147,9 +147,10 @@ tv_status tv_verify_attn(const tv_problem* p, const void* q, const void* kv_buf,
 
 /*
  * Measurement variant of tv_verify_attn: the same arguments and the same
- * kernels, plus two caller-created hipEvent_t handles recorded on `stream`
- * immediately before and after the split-attention kernel (the dominant one),
- * so a benchmark can time that kernel alone.  Either event may be NULL.
+ * kernels, plus two caller-created hipEvent_t handles (timing enabled) that
+ * take the start and end times of the split-attention kernel's own dispatch
+ * (the dominant kernel; hipExtLaunchKernel), so a benchmark can time that
+ * kernel alone without adding packets to `stream`.  Either event may be NULL.
  */
 tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* kv_buf,
                                const int32_t* kv_indices, const int32_t* kv_indptr,

@@ -199,9 +199,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
   sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
   const int grid = (int)lay.grid;
-  if (ev0 && hipEventRecord(ev0, s) != hipSuccess) return TV_ERR_LAUNCH;
-  if (tv::launch_split(sp, grid, p->out_dtype, s) != hipSuccess) return TV_ERR_LAUNCH;
-  if (ev1 && hipEventRecord(ev1, s) != hipSuccess) return TV_ERR_LAUNCH;
+  if (tv::launch_split(sp, grid, p->out_dtype, s, ev0, ev1) != hipSuccess) return TV_ERR_LAUNCH;
 
   if (lay.plan.merge) {
     tv::MergeParams mp;

@@ -84,7 +84,9 @@ struct MergeParams {
 };
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st);
-hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st);
+// ev0 / ev1 (may be null): stamped with the split kernel's own start and end.
+hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st, hipEvent_t ev0,
+                        hipEvent_t ev1);
 hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
                         hipStream_t st);
 

@@ -54,6 +54,7 @@
 //  * Prologue and epilogue run once per workgroup: accumulators are zeroed by
 //    MFMAs; the epilogue stages O through LDS in two buffers and stores rows
 //    as contiguous runs.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1093,9 +1094,12 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
 }
 
 // Launches go through hipLaunchKernel, which reports this launch's own status
-// (a non-gfx950 device fails here: the library carries gfx950 code only).
+// (a non-gfx950 device fails here: the library carries gfx950 code only).  With
+// events, hipExtLaunchKernel stamps them with the dispatch's own start and end
+// times: no separate marker packets enter the stream around the kernel.
 
-hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st) {
+hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st, hipEvent_t ev0,
+                        hipEvent_t ev1) {
   const uint16_t* q = p.q;
   const uint16_t* kv = p.kv;
   const int32_t* kvi = p.kv_indices;
@@ -1120,6 +1124,7 @@ hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st)
        {reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, false>),
         reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, true>)}}};
   const void* fn = fns[out == OUT_F32][p.wide][p.precise];
+  if (ev0 || ev1) return hipExtLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st, ev0, ev1, 0);
   return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }
 }  // namespace tv
