@@ -102,11 +102,17 @@ typedef struct tv_plan {
 tv_status tv_get_plan(const tv_problem* p, tv_plan* plan);
 
 /* Bytes of device workspace tv_verify_attn needs for `p` (0 if `p` is invalid
- * or there is nothing to compute).  It holds one 32-bit visibility word per
- * (draft token, 32-key tile) and, when more than one split is used, the
- * per-split partial outputs: total_q * H * max_splits entries of 512 fp16 values
- * plus two fp32 (lse, scale exponent), or with TV_FLAG_PRECISE_P of 512 + 1 fp32,
- * each part rounded up to 256 bytes. */
+ * or there is nothing to compute).  It holds, each part rounded up to 256
+ * bytes:
+ *  - one 32-bit visibility word per (draft token, 32-key tile), only when some
+ *    32 consecutive rows (draft * H + head, from a multiple of 32) span more
+ *    than 4 draft tokens (H < 8, H = 9); otherwise the kernels read the mask
+ *    bytes directly;
+ *  - when more than one split is used, the per-split partial outputs:
+ *    total_q * H * max_splits entries of 512 fp16 values plus two fp32 (lse,
+ *    scale exponent), or with TV_FLAG_PRECISE_P of 512 + 1 fp32;
+ *  - for a batch of more than one request, one int32 per work item (the
+ *    longest-first dispatch order). */
 size_t tv_workspace_bytes(const tv_problem* p);
 
 /*

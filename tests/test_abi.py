@@ -44,8 +44,28 @@ def test_plan_live_shape_is_one_split():
     pl = tv.plan(prob())
     assert pl["max_splits"] == 1 and pl["merge"] == 0 and pl["row_blocks"] == 1
     assert pl["split_keys"] % 32 == 0 and pl["split_keys"] >= 30
-    # visibility words only: 9 drafts x 1 tile x 4 bytes, 256-byte aligned
-    assert pl["workspace_bytes"] == 256 == tv.workspace_bytes(prob())
+    # one split, and the split kernel reads the mask bytes itself: no workspace
+    assert pl["workspace_bytes"] == 0 == tv.workspace_bytes(prob())
+    # at 3 heads a wave's rows span up to 12 drafts: packed visibility words,
+    # 9 drafts x 1 tile x 4 bytes, 256-byte aligned
+    assert tv.workspace_bytes(prob(num_heads=3)) == 256
+
+
+def drafts_spanned(n, H):
+    """Most draft tokens among the 32 rows of any wave of one request (brute force)."""
+    rows = n * H
+    return max(len({r // H for r in range(a, min(a + 32, rows))}) for a in range(0, rows, 32))
+
+
+@pytest.mark.parametrize("H", list(range(1, 21)) + [24, 48, 64, 128])
+def test_mask_bytes_mode_follows_the_draft_span(H):
+    # packed words (and so workspace) exactly when some wave spans more than 4 drafts
+    n = 40
+    p = prob(num_heads=H, total_q=n, max_q_len=n, total_kv=30 + n, max_kv_len=30 + n,
+             total_mask=n * (30 + n))
+    assert tv.plan(p)["max_splits"] == 1
+    words = -(-(n * 3 * 4) // 256) * 256
+    assert tv.workspace_bytes(p) == (words if drafts_spanned(n, H) > 4 else 0)
 
 
 def test_plan_explicit_splits_cover_the_longest_request():
@@ -57,7 +77,7 @@ def test_plan_explicit_splits_cover_the_longest_request():
     assert (pl["max_splits"] - 1) * pl["split_keys"] < 32800
     assert pl["max_splits"] <= 32 and pl["merge"] == 1 and pl["row_blocks"] == 4
     rows = 32 * 16
-    words = -(-(32 * 1025 * 4) // 256) * 256
+    words = 0  # 16 heads: each wave's rows are 2 drafts, the mask is read as bytes
 
     def parts(out_bytes, lse_bytes):
         return -(-(rows * pl["max_splits"] * 512 * out_bytes) // 256) * 256 + \
@@ -123,7 +143,7 @@ def test_bad_shapes_are_rejected():
 
 
 def test_null_pointers_and_short_workspace_fail_before_any_launch():
-    p = prob()
+    p = prob(num_heads=3)  # packed visibility words: 256 bytes of workspace
     fake = 1 << 20  # aligned non-null stand-in; never dereferenced on these paths
     args = [fake] * 7
     # q missing

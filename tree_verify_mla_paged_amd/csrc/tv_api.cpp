@@ -37,6 +37,19 @@ constexpr int kMinSplitTiles = 4;  // keys per split >= 128 unless the caller as
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// Whether the 32 rows (draft * H + head) of every wave, rows 32k .. 32k + 31 of
+// a request, span at most MASK_BYTES_DRAFTS draft tokens.  The span depends on
+// 32k mod H only, so k < H covers every case; a request's last wave has fewer
+// rows and no wider a span.
+bool waves_span_few_drafts(int64_t rows_max, int64_t H) {
+  const int64_t waves = std::min<int64_t>(ceil_div(rows_max, 32), H);
+  for (int64_t k = 0; k < waves; ++k) {
+    const int64_t a = 32 * k, z = std::min<int64_t>(a + 31, rows_max - 1);
+    if (z / H - a / H + 1 > tv::MASK_BYTES_DRAFTS) return false;
+  }
+  return true;
+}
+
 struct Layout {
   tv_plan plan;
   int32_t max_tiles;     // 32-key tiles of the longest request
@@ -45,6 +58,7 @@ struct Layout {
   int64_t wsl_off, wsl_bytes;
   int64_t order_off, order_bytes;  // longest-first work order (0 bytes: natural order)
   int32_t xcd_group;     // dispatch positions per XCD group
+  bool mask_bytes;       // the split kernel reads the mask bytes (no packed words)
   int64_t grid;          // split-kernel workgroups
   bool active;           // anything to compute
 };
@@ -94,8 +108,9 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   lay->grid = ceil_div(total_work, 8 * lay->xcd_group) * 8 * lay->xcd_group;
 
   lay->max_tiles = (int32_t)std::max<int64_t>(1, ceil_div(L, tv::TILE_KEYS));
+  lay->mask_bytes = waves_span_few_drafts(rows_max, p->num_heads);
   lay->words_off = 0;
-  lay->words_bytes = align256(p->total_q * lay->max_tiles * 4);
+  lay->words_bytes = lay->mask_bytes ? 0 : align256(p->total_q * lay->max_tiles * 4);
   int64_t off = lay->words_bytes;
   if (max_splits > 1) {
     // partial outputs: fp32 in precise mode, else fp16 with a scale exponent
@@ -153,7 +168,11 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* words = reinterpret_cast<uint32_t*>(ws + lay.words_off);
 
-  if (p->max_kv_len > 0) {
+  // the pack kernel: visibility words (waves spanning more draft tokens than
+  // the split kernel reads bytes for) and the longest-first order (batches);
+  // neither needed, no launch
+  const bool want_order = lay.order_bytes > 0;
+  if (p->max_kv_len > 0 && (!lay.mask_bytes || want_order)) {
     tv::PackParams pp;
     pp.mask = mask;
     pp.mask_indptr = mask_indptr;
@@ -169,7 +188,10 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     pp.num_heads = p->num_heads;
     pp.batch = p->batch;
     // a wave per draft row and 512 keys (tv_pack_mask_kernel), 4 waves per workgroup
-    const int64_t gx = ceil_div((int64_t)p->max_q_len * ceil_div(p->max_kv_len, tv::PACK_KEYS), 4);
+    const int64_t gx =
+        lay.mask_bytes
+            ? 0
+            : ceil_div((int64_t)p->max_q_len * ceil_div(p->max_kv_len, tv::PACK_KEYS), 4);
     if (gx + 1 > kMaxInt32) return TV_ERR_SHAPE;
     pp.sched_block = pp.order ? (int32_t)gx : -1;  // one more workgroup column
     if (tv::launch_pack(pp, (int)gx + (pp.order ? 1 : 0), p->batch, s) != hipSuccess)
@@ -182,7 +204,9 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.kv_indices = kv_indices;
   sp.kv_indptr = kv_indptr;
   sp.qo_indptr = qo_indptr;
-  sp.mask_words = words;
+  sp.mask = mask;
+  sp.mask_indptr = mask_indptr;
+  sp.mask_words = lay.mask_bytes ? nullptr : words;
   sp.order = lay.order_bytes ? reinterpret_cast<const int32_t*>(ws + lay.order_off) : nullptr;
   sp.out = out;
   sp.lse = lse;
@@ -196,10 +220,13 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.s.total_work = (int32_t)((int64_t)p->batch * lay.plan.max_splits * lay.plan.row_blocks);
   sp.s.max_tiles = lay.max_tiles;
   sp.s.xcd_group = lay.xcd_group;
+  sp.s.mask_bytes = lay.mask_bytes ? 1 : 0;
+  sp.s.total_mask = (int32_t)p->total_mask;
+  sp.s.out_f32 = p->out_dtype == TV_OUT_F32 ? 1 : 0;
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
   sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
   const int grid = (int)lay.grid;
-  if (tv::launch_split(sp, grid, p->out_dtype, s, ev0, ev1) != hipSuccess) return TV_ERR_LAUNCH;
+  if (tv::launch_split(sp, grid, s, ev0, ev1) != hipSuccess) return TV_ERR_LAUNCH;
 
   if (lay.plan.merge) {
     tv::MergeParams mp;

@@ -19,6 +19,10 @@ constexpr int VD = 512;           // value dims
 constexpr int ROWS_PER_WG = 128;  // query rows (draft x head) per workgroup: 4 waves x 32
 constexpr int TILE_KEYS = 32;     // keys per LDS tile
 constexpr int PACK_KEYS = 512;    // keys of a draft row one wave of tv_pack_mask_kernel packs
+// When every wave's 32 rows span at most this many draft tokens, the split
+// kernel reads their mask bytes itself (two drafts per wave-wide byte load and
+// ballot); otherwise tv_pack_mask_kernel packs visibility words first.
+constexpr int MASK_BYTES_DRAFTS = 4;
 constexpr int OUT_BF16 = 0;
 constexpr int OUT_F32 = 1;
 
@@ -48,6 +52,10 @@ struct SplitScalars {
   int32_t total_work;         // batch * max_splits * row_blocks
   int32_t max_tiles;
   int32_t xcd_group;          // dispatch positions per XCD group (see tv_split_kernel)
+  int32_t mask_bytes;         // 1: visibility read from the mask bytes in the tile loop
+                              // (see MASK_BYTES_DRAFTS); 0: from tv_pack_mask_kernel's words
+  int32_t total_mask;         // bytes of the mask (its buffer's record count)
+  int32_t out_f32;            // output dtype: 1 fp32, 0 bf16
 };
 
 struct SplitParams {
@@ -56,7 +64,9 @@ struct SplitParams {
   const int32_t* kv_indices;
   const int32_t* kv_indptr;
   const int32_t* qo_indptr;
-  const uint32_t* mask_words; // [total_q, max_tiles] from tv_pack_mask_kernel
+  const uint8_t* mask;        // the caller's mask bytes (mask_bytes mode)
+  const int32_t* mask_indptr;
+  const uint32_t* mask_words; // [total_q, max_tiles] from tv_pack_mask_kernel (word mode)
   const int32_t* order;       // longest-first work order from tv_pack_mask_kernel, or null
   void* out;                  // [total_q, H, 512] bf16 or fp32 (requests with one split)
   float* lse;                 // [total_q, H]
@@ -85,7 +95,7 @@ struct MergeParams {
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st);
 // ev0 / ev1 (may be null): stamped with the split kernel's own start and end.
-hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st, hipEvent_t ev0,
+hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1);
 hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
                         hipStream_t st);

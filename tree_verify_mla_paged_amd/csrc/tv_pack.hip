@@ -4,8 +4,9 @@
 // each request's block (page 2 "Flipping the Switch", section "The Long Road to
 // Parity": mask=(270,) for 9 drafts x 30 keys; page 3 "The Pivot to Live
 // Cutover", section "The Technical Investigation": the block of request b is
-// located through mask_indptr).  The split kernel reads it as one 32-bit word
-// per (draft token, 32-key tile), built here with wave ballots.
+// located through mask_indptr).  When a wave's rows span more draft tokens
+// than the split kernel reads mask bytes for, it reads one 32-bit word per
+// (draft token, 32-key tile) instead, built here with wave ballots.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

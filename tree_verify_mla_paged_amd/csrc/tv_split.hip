@@ -94,6 +94,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // ---------------------------------------------------------------- split kernel
 
+// Mask bytes of one tile for one wave (byte mode): 2 loads, 4 draft tokens.
+constexpr int MASK_J = 2;
+static_assert(2 * MASK_J == MASK_BYTES_DRAFTS, "");
+struct MaskBytes {
+  uint32_t b[MASK_J];
+};
+
 // Everything a workgroup needs to gather and consume tiles of its KV split.
 struct SplitCtx {
   const uint16_t* kv;
@@ -111,8 +118,23 @@ struct SplitCtx {
   int rp_off[4];
   uint32_t al_off;          // this lane's row in a rescale-factor buffer (bytes)
   bool row_ok;
+  uint32_t rowm;            // row_ok as a mask: all ones or 0
   float scale_log2;
   lds_u8* sring;            // this wave's ring of gather slots: SLOT_RING entries of 256 bytes
+  // Visibility straight from the mask bytes (mbytes: the wave's rows span at
+  // most 2 * MASK_J draft tokens): the request's mask at key kbeg of its draft
+  // 0 and the bytes of the buffer from there (0 without byte mode); this
+  // lane's offset for byte load 0 (draft first + lane / 32, key lane % 32)
+  // and the step between loads (2 drafts); for the draft of the lane's row,
+  // d = draft - first: the load holding it (dpair = d / 2) and the ballot half
+  // (dhalf = 32 * (d % 2)).  Otherwise the words of tv_pack_mask_kernel,
+  // gathered with the tile (wbase / wvoff).
+  const uint8_t* mrow;
+  int mrec;
+  uint32_t mvoff, mstep;
+  uint32_t dhalf;
+  bool dpair;
+  bool mbytes;
 };
 
 // Direct-to-LDS gathers, as inline asm: the compiler treats the equivalent
@@ -236,7 +258,8 @@ __device__ __forceinline__ GatherDst gather_dst(const lds_u8* sb, const SplitCtx
 //   piece 0..7: latent dims 0..511 of key 8*wave + j, to stage + (8*wave + j)*ROW
 //               + key_shift(8*wave + j) = main + j*ROW + 16*(j >> 2);
 //   piece 8:    RoPE dims of the wave's 8 keys (one slot per 8 lanes);
-//   piece 9:    the visibility words of the tile (one per draft row).
+//   piece 9:    the visibility words of the tile (one per draft row), unless
+//               the mask bytes are read directly (mask_load).
 // WIDE: the pool may exceed 4 GiB, so the gathers use 64-bit addresses.  The
 // slots are taken by reference to the caller's array (a pointer kept in a
 // struct makes the compiler move the array to memory).
@@ -255,7 +278,7 @@ __device__ __forceinline__ void gather_piece(const GatherDst& g, const int (&slo
       dma_row_v(g.rope, slane, c.rp_voff, c);
     }
   } else {
-    dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1), g.mask);
+    if (!c.mbytes) dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1), g.mask);
   }
 }
 
@@ -332,13 +355,43 @@ __device__ __forceinline__ f32x16 qk_tile(const lds_u8* sb, const bf16x8 (&qf)[Q
   return acc;
 }
 
-// Visibility of the lane's row over tile t (bit k = key kbeg + 32*t + k).
-__device__ __forceinline__ uint32_t tile_mask(const lds_u8* sb, const SplitCtx& c, int t) {
-  const int rem = c.kend - (c.kbeg + t * TILE);
-  const uint32_t valid = rem >= TILE ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
-  const uint32_t w =
-      *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(sb + c.mw_off);
-  return c.row_ok ? (w & valid) : 0u;
+// Visibility of the lane's row over tile t (bit k = key kbeg + 32*t + k): the
+// keys of the split only, nothing for a row past the request.
+__device__ __forceinline__ uint32_t tile_valid(const SplitCtx& c, int t);
+__device__ __forceinline__ uint32_t mask_finish(uint32_t w, const SplitCtx& c, int t) {
+  return w & tile_valid(c, t) & c.rowm;
+}
+// The lane's gathered word of tile t, unfinished (word mode).
+__device__ __forceinline__ uint32_t tile_word(const lds_u8* sb, const SplitCtx& c) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(sb + c.mw_off);
+}
+
+// The mask bytes one wave needs for a tile: load j holds key lane % 32 of
+// draft first + 2j + lane / 32 (per lane, 0 = hidden).  They are read through a
+// buffer resource whose record count ends at the mask's last byte (0 records
+// without byte mode), so lanes past the request's drafts or keys read another
+// request's bytes or zeros (out of range), never outside the mask; their bits
+// are never used.  The loads and ballots are unconditional: a load under a
+// branch makes the compiler merge its result with the old value by a copy,
+// which waits for every load in flight, the tile gathers included.
+__device__ __forceinline__ void mask_load(MaskBytes& m, const SplitCtx& c, int t) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(c.mrow + TILE * t), (short)0, max(c.mrec - TILE * t, 0), 0x00020000);
+#pragma unroll
+  for (int j = 0; j < MASK_J; ++j)
+    m.b[j] = __builtin_amdgcn_raw_buffer_load_b8(r, c.mvoff + j * c.mstep, 0, 0);
+}
+// The word from the loaded bytes: a ballot per load gives the words of two
+// drafts (lanes 0..31, 32..63); each lane shifts its draft's half out of the
+// ballot of its pair of drafts.
+__device__ __forceinline__ uint32_t mask_word(const MaskBytes& m, const SplitCtx& c, int t) {
+  static_assert(MASK_J == 2, "");
+  const unsigned long long b0 = __ballot(m.b[0] != 0);
+  const unsigned long long b1 = __ballot(m.b[1] != 0);
+  const uint32_t x = (uint32_t)(b0 >> c.dhalf), y = (uint32_t)(b1 >> c.dhalf);
+  // a row past the request keeps its (clamped) draft's visibility: it writes
+  // nothing, and its scores, of zero queries, stay finite
+  return (c.dpair ? y : x) & tile_valid(c, t);
 }
 
 // QK chain of one tile (as qk_tile) calling bg(ks) after the MFMA of each
@@ -402,13 +455,26 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 template <bool PRECISE>
 __device__ __forceinline__ void write_p(lds_u8* pb, const SplitCtx& c, const Soft& sm);
 
+// A tile's visibility before the choice between its sources, made in the
+// softmax's first step: the gathered word unfinished (ww) with the tile's key
+// range (valid), or the word from the mask bytes, finished (wb).
+struct MaskSel {
+  uint32_t ww, wb, valid;
+};
+__device__ __forceinline__ uint32_t tile_valid(const SplitCtx& c, int t) {
+  const int rem = c.kend - (c.kbeg + t * TILE);
+  return rem >= TILE ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
+}
+
 // alpha_u: the LDS address of the tile's rescale factors; pb_u: its P buffer.
 template <bool PRECISE>
-__device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, uint32_t mw,
+__device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, MaskSel& ms,
                                           const SplitCtx& c, float& m_ref, float& l_sum,
                                           uint32_t alpha_u, lds_u8* pb_u) {
   if (step == 0) {
     fence(S);
+    fence(ms.ww);
+    const uint32_t mw = c.mbytes ? ms.wb : (ms.ww & ms.valid & c.rowm);
     // a tile every row of the wave sees whole (every prefix tile) skips this
     // uniform branch; masked scores are -inf
     if (!__all(mw == 0xffffffffu)) {
@@ -676,18 +742,20 @@ __device__ __forceinline__ void split_slots(const SplitCtx& c) {
   slot_dma(c, 1);
   slot_dma(c, 2);
 }
-// split_gathers: once the slots have landed, the gathers of tiles 0 and 1.  QN
-// is the number of vector loads issued since split_slots (the wave's query
-// loads): waiting until at most QN are outstanding covers the three slot loads
-// and leaves the query rows in flight.
-template <bool WIDE, int QN>
-__device__ __forceinline__ void split_gathers(lds_u8* stages, const SplitCtx& c) {
+// split_gathers: once the slots have landed (the caller waits), the gathers of
+// tiles 0 and 1 and their mask bytes.
+template <bool WIDE>
+__device__ __forceinline__ void split_gathers(lds_u8* stages, const SplitCtx& c, MaskBytes& m0,
+                                              MaskBytes& m1) {
   int slot[8];
   SlotRaw r;
-  wait_vmcnt<QN>();
   slot_load(r, c, 0);
   slot_take(slot, r, 0);
   slot_take(slot, r, 1);
+  if (c.mbytes) {
+    mask_load(m0, c, 0);
+    mask_load(m1, c, 1);  // (past the split: real bytes or zeros, unused)
+  }
   issue_tile<WIDE>(stages, slot, r.slane, c, 0);
   if (c.ntiles > 1) {
     slot_load(r, c, 1);
@@ -711,12 +779,17 @@ __device__ __forceinline__ int alpha_moved(float a0, float a1) {
 // Iteration t's QK chain (tile t+1, stage nx1) with, in its shadow: the read
 // of tile t's rescale factors; if GATHER, the slots and gathers of tile t+2
 // (stage nx2) and the slots of tile t+3; then tile t+1's visibility words and
-// the first PV operands of tile t (stage cur).
+// the first PV operands of tile t (stage cur).  Tile t+1's visibility comes
+// back as mww (the gathered word, unfinished) and mwb (from the mask bytes: mb
+// holds tile t+1's, turned into the word early in the chain, and then receives
+// tile t+2's); the softmax's first step picks one (MaskSel), so that nothing
+// in the chain waits for the word's LDS read.
 template <bool WIDE, bool PRECISE, bool GATHER>
 __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
                                            const bf16x8 (&qf)[QK / 16], const float* alpha_t,
-                                           int t, int cur, int nx1, int nx2, uint32_t& mw,
-                                           int& resc, bf16x8 (&A0)[2]) {
+                                           int t, int cur, int nx1, int nx2, uint32_t& mww,
+                                           uint32_t& mwb, int& resc, bf16x8 (&A0)[2],
+                                           MaskBytes& mb) {
   constexpr int G0 = 5;  // first gather piece; then one every third k-step
   static_assert(G0 + 3 * (DMA_PER_TILE - 1) + 2 < QK / 16, "");
   SlotRaw r;
@@ -733,14 +806,19 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
       alpha_load(a0, a1, alpha_t, c);
     } else if (ks == 2 || ks == 3) {
       if (GATHER) slot_take(slot, r, ks - 2);
+      if (ks == 3 && c.mbytes) {
+        mwb = mask_word(mb, c, t + 1);  // tile t+1's bytes
+        fence(mwb);  // here, in the chain's shadow, not where it is used
+      }
     } else if (ks == 4) {
       fence(a0);
       fence(a1);
       resc = alpha_moved(a0, a1);
     } else if (ks >= G0 && ks < G0 + 3 * DMA_PER_TILE && (ks - G0) % 3 == 0) {
       if (GATHER) gather_piece_n<WIDE>((ks - G0) / 3, g, slot, r.slane, c, t + 2);
+      if (GATHER && ks == G0 + 3 * (DMA_PER_TILE - 1) && c.mbytes) mask_load(mb, c, t + 2);
     } else if (ks == G0 + 3 * DMA_PER_TILE - 2) {
-      mw = tile_mask(stages + nx1 * STAGE, c, t + 1);
+      if (!c.mbytes) mww = tile_word(stages + nx1 * STAGE, c);
     } else if (ks == G0 + 3 * DMA_PER_TILE - 1) {
       pv_a_first<PRECISE>(A0, stages + cur * STAGE, c);
     }
@@ -761,13 +839,15 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
 template <bool WIDE, bool PRECISE>
 __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds_u8* pbuf,
                                           bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
-                                          float& m_ref, float& l_sum, float* alpha_s) {
+                                          float& m_ref, float& l_sum, float* alpha_s,
+                                          const MaskBytes& m0, MaskBytes& mb) {
   constexpr int PB = PRECISE ? 2 * PBUF_LO : PBUF_LO;  // bytes of one P buffer
   const int nt = c.ntiles;
   const uint32_t alpha_lds = lds_addr((lds_u8*)alpha_s);
   // tile 0: its gathers landed, and with them the query loads issued before
-  // them (only tile 1's gathers may be outstanding); QK, softmax
-  if (nt > 1) wait_vmcnt<DMA_PER_TILE>();
+  // them (only tile 1's nine row gathers may be outstanding; each load the
+  // compiler sees, such as the mask bytes, it waits for itself); QK, softmax
+  if (nt > 1) wait_vmcnt<DMA_PER_TILE - 1>();
   else wait_vmcnt<0>();
   __syncthreads();
   Soft sm;
@@ -779,27 +859,35 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
     // each QK MFMA, which in steady state waits out the tile gathers instead
 #pragma unroll
     for (int ks = 0; ks < QK / 16; ++ks) asm volatile("" : "+v"(qf[ks]));
-    const uint32_t mw = tile_mask(stages, c, 0);
+    MaskSel ms{0u, 0u, tile_valid(c, 0)};
+    if (c.mbytes) ms.wb = mask_word(m0, c, 0);
+    else ms.ww = tile_word(stages, c);
 #pragma unroll
     for (int st = 0; st < SOFT_STEPS; ++st)
-      soft_step<PRECISE>(st, sm, S, mw, c, m_ref, l_sum, alpha_lds, pbuf);
+      soft_step<PRECISE>(st, sm, S, ms, c, m_ref, l_sum, alpha_lds, pbuf);
   }
   int cur = 0;  // stage of tile t
   for (int t = 0; t < nt; ++t) {
     const int nx1 = cur == NSTAGE - 1 ? 0 : cur + 1;  // stage of tile t+1
     const int nx2 = cur == 0 ? NSTAGE - 1 : cur - 1;  // stage of tile t+2
-    if (t + 1 < nt) wait_vmcnt<0>();
+    // (unconditional: on the last iteration nothing is in flight, and the
+    // compiler then knows every load it issued has landed here)
+    wait_vmcnt<0>();
     __syncthreads();
     const float* alpha_t = alpha_s + ROWS_PER_WG * (t & 1);
     f32x16 S;
-    uint32_t mw = 0;  // tile t+1's visibility (none past the last tile)
+    // tile t+1's visibility (none past the last tile)
+    MaskSel ms{0u, 0u, 0u};
     int resc;         // some row's reference moved in tile t
     bf16x8 A0[2];
     if (t + 2 < nt) {
-      S = qk_phase<WIDE, PRECISE, true>(stages, c, qf, alpha_t, t, cur, nx1, nx2, mw, resc, A0);
+      S = qk_phase<WIDE, PRECISE, true>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww, ms.wb,
+                                        resc, A0, mb);
+      ms.valid = tile_valid(c, t + 1);
     } else if (t + 1 < nt) {
-      S = qk_phase<WIDE, PRECISE, false>(stages, c, qf, alpha_t, t, cur, nx1, nx2, mw, resc,
-                                         A0);
+      S = qk_phase<WIDE, PRECISE, false>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww, ms.wb,
+                                         resc, A0, mb);
+      ms.valid = tile_valid(c, t + 1);
     } else {
       float a0, a1;
       alpha_load(a0, a1, alpha_t, c);
@@ -814,7 +902,7 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
 #pragma unroll
                        for (int st = 0; st < SOFT_STEPS; ++st)
                          if (i == soft_at<PRECISE>(st))
-                           soft_step<PRECISE>(st, sm, S, mw, c, m_ref, l_sum, alpha_n, pb_n);
+                           soft_step<PRECISE>(st, sm, S, ms, c, m_ref, l_sum, alpha_n, pb_n);
                      });
     cur = nx1;
   }
@@ -862,11 +950,12 @@ __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
 }
 
-template <int OUT, bool WIDE, bool PRECISE>
+template <bool WIDE, bool PRECISE, bool MASKB>
 __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
-    const int32_t* __restrict__ qo_indptr_, const uint32_t* __restrict__ mask_words_,
+    const int32_t* __restrict__ qo_indptr_, const uint8_t* __restrict__ mask_,
+    const int32_t* __restrict__ mask_indptr_, const uint32_t* __restrict__ mask_words_,
     const int32_t* __restrict__ order_, void* __restrict__ out_, float* __restrict__ lse_,
     void* __restrict__ ws_o_, float* __restrict__ ws_lse_, SplitScalars p) {
   // one LDS block: the tile stages, then the two P buffers (the epilogue's two
@@ -928,6 +1017,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   // this lane's query row
   const int r = row0 + wave * 32 + l32;
   c.row_ok = r < R;
+  c.rowm = c.row_ok ? 0xffffffffu : 0u;
   const int dl = c.row_ok ? r / H - i0 : 0;
   const int64_t g = (int64_t)q0 * H + r;  // global row = token * H + head
   // visibility words of draft i0 + d, tile 0 of the split: row (q0 + i0 + d)
@@ -957,6 +1047,19 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
                32 * ((lane >> 4) & 1) + 8 * (sl & 3);
   }
   c.mw_off = MAIN_BYTES + ROPE_BYTES + 4 * dl;
+  c.mbytes = MASKB;  // a constant: every branch on it folds
+  {
+    // the first draft of the wave's rows (a wave past the request's rows: its last)
+    const int first = min(row0 + 32 * wave, R - 1) / H;
+    const int64_t moff = (int64_t)mask_indptr_[b] + c.kbeg;
+    c.mrow = mask_ + moff;
+    c.mrec = c.mbytes ? (int)((int64_t)p.total_mask - moff) : 0;
+    c.mvoff = (uint32_t)(first + half) * (uint32_t)L + (uint32_t)l32;
+    c.mstep = 2u * (uint32_t)L;
+    const int d = min(r, R - 1) / H - first;  // < MASK_BYTES_DRAFTS in byte mode
+    c.dpair = d >= 2;
+    c.dhalf = 32u * (uint32_t)(d & 1);
+  }
 
   // prologue: the slot loads, then the query rows (their transfer overlaps the
   // slots' round trip), then the first two tiles' gathers
@@ -971,14 +1074,17 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   const bool wave_q = row0 + wave * 32 < R;
 #pragma unroll
   for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = bf16x8{};
+  MaskBytes m0 = {}, mb = {};  // mask bytes of tiles 0 and 1 (byte mode)
   if (c.ntiles > 0) {
     if (c.row_ok) {
       const bf16x8* qp = reinterpret_cast<const bf16x8*>(q_ + g * QK + half * 8);
 #pragma unroll
       for (int ks = 0; ks < QK / 16; ++ks) qf[ks] = qp[2 * ks];
     }
-    if (wave_q) split_gathers<WIDE, QK / 16>(stages, c);
-    else split_gathers<WIDE, 0>(stages, c);
+    // the slots have landed once at most the query loads are outstanding
+    if (wave_q) wait_vmcnt<QK / 16>();
+    else wait_vmcnt<0>();
+    split_gathers<WIDE>(stages, c, m0, mb);
   }
 
   // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
@@ -988,7 +1094,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
   if (c.ntiles > 0)
-    run_split<WIDE, PRECISE>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s);
+    run_split<WIDE, PRECISE>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s, m0, mb);
 
   // the last PV MFMAs must finish before O is read out of the AGPRs
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -1065,7 +1171,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
           if (si == 0) ws_lse_[2 * wi + 1] = (float)(e - 15);
         }
       } else if (live) {
-        if (nsplit > 1 || OUT == OUT_F32) {
+        if (nsplit > 1 || p.out_f32) {
           float* o = nsplit > 1 ? static_cast<float*>(ws_o_) + (gr * p.max_splits + s) * VD
                                 : static_cast<float*>(out_) + gr * VD;
           o += 8 * si;
@@ -1098,13 +1204,15 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
 // events, hipExtLaunchKernel stamps them with the dispatch's own start and end
 // times: no separate marker packets enter the stream around the kernel.
 
-hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st, hipEvent_t ev0,
+hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1) {
   const uint16_t* q = p.q;
   const uint16_t* kv = p.kv;
   const int32_t* kvi = p.kv_indices;
   const int32_t* kvp = p.kv_indptr;
   const int32_t* qop = p.qo_indptr;
+  const uint8_t* mk = p.mask;
+  const int32_t* mkp = p.mask_indptr;
   const uint32_t* mw = p.mask_words;
   const int32_t* ord = p.order;
   void* o = p.out;
@@ -1112,18 +1220,18 @@ hipError_t launch_split(const SplitParams& p, int grid, int out, hipStream_t st,
   void* wo = p.ws_o;
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
-  void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mw, &ord, &o, &l, &wo, &wl, &sc};
-  // [out dtype][wide][precise]
+  void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mk, &mkp, &mw, &ord, &o, &l, &wo, &wl, &sc};
+  // [wide][precise][mask bytes]
   static const void* const fns[2][2][2] = {
-      {{reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, false, true>)},
-       {reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, true, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<OUT_BF16, true, true>)}},
-      {{reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, false, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, false, true>)},
-       {reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<OUT_F32, true, true>)}}};
-  const void* fn = fns[out == OUT_F32][p.wide][p.precise];
+      {{reinterpret_cast<const void*>(&tv_split_kernel<false, false, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<false, false, true>)},
+       {reinterpret_cast<const void*>(&tv_split_kernel<false, true, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<false, true, true>)}},
+      {{reinterpret_cast<const void*>(&tv_split_kernel<true, false, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<true, false, true>)},
+       {reinterpret_cast<const void*>(&tv_split_kernel<true, true, false>),
+        reinterpret_cast<const void*>(&tv_split_kernel<true, true, true>)}}};
+  const void* fn = fns[p.wide][p.precise][p.s.mask_bytes != 0];
   if (ev0 || ev1) return hipExtLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st, ev0, ev1, 0);
   return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }
