@@ -29,9 +29,11 @@ constexpr int PACK_SEGS = PACK_KEYS / 64;
 // the hardware dispatching workgroups in position order as compute units free
 // up, this is greedy longest-processing-time scheduling.
 __device__ void schedule_work(const PackParams& p) {
+  constexpr int PER = SCHED_BUCKETS / 256;  // buckets per thread in the scan
+  static_assert(SCHED_BUCKETS % 256 == 0, "");
   __shared__ int cnt[SCHED_BUCKETS];
+  __shared__ int wsum[4];
   const int t = threadIdx.x;
-  for (int i = t; i < p.total_work; i += 256) p.order[i] = -1;
   for (int i = t; i < SCHED_BUCKETS; i += 256) cnt[i] = 0;
   __syncthreads();
   const int units = p.batch * p.max_splits;
@@ -52,14 +54,32 @@ __device__ void schedule_work(const PackParams& p) {
     if (rbs > 0) atomicAdd(&cnt[bucket], rbs);
   }
   __syncthreads();
-  if (t == 0) {  // exclusive prefix sum, longest class first
-    int run = 0;
-    for (int i = 0; i < SCHED_BUCKETS; ++i) {
-      const int c = cnt[i];
-      cnt[i] = run;
-      run += c;
-    }
+  // exclusive prefix sum over the buckets, longest class first: each thread
+  // scans PER consecutive buckets, the wave scans its threads' totals, the
+  // workgroup adds the totals of the waves before
+  int v[PER];
+  int run = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    v[k] = run;
+    run += cnt[PER * t + k];
   }
+  const int lane = t & 63, wave = t >> 6;
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) cnt[PER * t + k] = base + v[k];
+  // positions past the existing work items hold -1
+  for (int i = total + t; i < p.total_work; i += 256) p.order[i] = -1;
   __syncthreads();
   for (int u = t; u < units; u += 256) {
     int bucket;
