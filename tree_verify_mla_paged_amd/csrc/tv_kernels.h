@@ -97,7 +97,8 @@ hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t s
 // ev0 / ev1 (may be null): stamped with the split kernel's own start and end.
 hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1);
+// many: 1024 threads per row (a single request split many ways), else 256.
 hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
-                        hipStream_t st);
+                        bool many, hipStream_t st);
 
 }  // namespace tv

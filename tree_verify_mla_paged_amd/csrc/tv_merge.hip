@@ -15,39 +15,44 @@
 
 namespace tv {
 
-// One row per workgroup, in chunks of up to MERGE_CHUNK splits.  A thread's
-// first U partial-output loads go out before anything else; meanwhile the
-// chunk's split LSEs are read once, cooperatively, and turned into weights in
-// LDS.  Each load is 16 bytes: a
-// thread owns DPT value dims (8 fp16 or 4 fp32), so a split's row takes TPS
-// threads and the workgroup's NPH = 256 / TPS phases take alternate splits,
-// combined through LDS at the end.  Weights are relative to the running
-// maximum M and are rescaled when a later chunk raises it.
+// One row per workgroup of NT threads (256, or 1024 for rows of many splits),
+// in chunks of up to MERGE_CHUNK splits.  A thread's first U partial-output
+// loads go out before anything else; meanwhile the chunk's split LSEs are read
+// once, cooperatively, and turned into weights in LDS.  Each load is 16 bytes:
+// a thread owns DPT value dims (8 fp16 or 4 fp32), so a split's row takes TPS
+// threads and the workgroup's NPH = NT / TPS phases take alternate splits,
+// combined through LDS at the end: NPH * U splits are in flight at once (64 or
+// 256 with fp16 partials), so a row of a long single request is read in one
+// round trip.  Weights are relative to the running maximum M and are rescaled
+// when a later chunk raises it.
 constexpr int MERGE_CHUNK = 1024;
 
-// Maximum over the workgroup (256 threads); ends with a barrier.
+// Maximum over the workgroup (NT threads); ends with a barrier.
+template <int NT>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  v = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) v = fmaxf(v, red[w]);
   __syncthreads();
   return v;
 }
 
-template <int OUT, bool F16P>
-__global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
+template <int OUT, bool F16P, int NT>
+__global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   constexpr int U = 16;               // loads per thread in flight
   constexpr int DPT = F16P ? 8 : 4;  // value dims per thread: one 16-byte load
   constexpr int TPS = VD / DPT;      // threads per split row
-  constexpr int NPH = 256 / TPS;     // splits in flight across the workgroup
+  constexpr int NPH = NT / TPS;      // splits in flight across the workgroup
   typedef float accv __attribute__((ext_vector_type(DPT)));
   __shared__ float wgt_s[MERGE_CHUNK];               // w_s
   __shared__ float wnum_s[F16P ? MERGE_CHUNK : 1];   // w_s 2^k_s
   __shared__ accv part_o[NPH - 1][TPS];
   __shared__ float part_w[NPH - 1][TPS];
-  __shared__ float red[4];
+  __shared__ float red[NT / 64];
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
   const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
@@ -85,12 +90,12 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
     const int nc = min(MERGE_CHUNK, ns - c0);
     load_batch(c0, h);
     float m = -INFINITY;
-    for (int i = t; i < nc; i += 256) {
+    for (int i = t; i < nc; i += NT) {
       const float lv = ls[LS * (c0 + i)];
       wgt_s[i] = lv;
       m = fmaxf(m, lv);
     }
-    const float Mn = fmaxf(M, block_max(m, red));
+    const float Mn = fmaxf(M, block_max<NT>(m, red));
     if (Mn == -INFINITY) continue;  // every split so far is empty (uniform)
     if (Mn > M) {
       // (w_s and w_s 2^k_s share the factor)
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
       W *= f;
       M = Mn;
     }
-    for (int i = t; i < nc; i += 256) {
+    for (int i = t; i < nc; i += NT) {
       const float w = __expf(wgt_s[i] - M);  // exp(-inf) = 0
       wgt_s[i] = w;
       if (F16P) wnum_s[i] = __builtin_ldexpf(w, (int)ls[LS * (c0 + i) + 1]);
@@ -155,16 +160,20 @@ __global__ __launch_bounds__(256) void tv_merge_kernel(MergeParams p) {
 }
 
 hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
-                        hipStream_t st) {
+                        bool many, hipStream_t st) {
   MergeParams a = p;
   void* args[] = {&a};
-  // [out dtype][fp16 partials]
-  static const void* const fns[2][2] = {
-      {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false>),
-       reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true>)},
-      {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false>),
-       reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true>)}};
-  const void* fn = fns[out == OUT_F32][f16_parts];
-  return hipLaunchKernel(fn, dim3(grid_x, batch), dim3(256), args, 0, st);
+  // [out dtype][fp16 partials][1024 threads]
+  static const void* const fns[2][2][2] = {
+      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 256>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 1024>)},
+       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 256>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 1024>)}},
+      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 256>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 1024>)},
+       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 256>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 1024>)}}};
+  const void* fn = fns[out == OUT_F32][f16_parts][many];
+  return hipLaunchKernel(fn, dim3(grid_x, batch), dim3(many ? 1024 : 256), args, 0, st);
 }
 }  // namespace tv
