@@ -240,11 +240,12 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     mp.split_keys = lay.plan.split_keys;
     mp.max_splits = lay.plan.max_splits;
     const int64_t gx = (int64_t)p->max_q_len * p->num_heads;  // one row per workgroup
-    // a single request split more ways than 256 threads keep in flight (16
-    // loads of 16 bytes each: 64 fp16 or 32 fp32 partial rows) gets 1024
-    // threads per row: each row is then read in one round trip
-    const bool many = p->batch == 1 && lay.plan.max_splits > (sp.precise ? 32 : 64);
-    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, many, s) !=
+    // few rows split many ways (a long single request with few heads): each
+    // row's value dims in 4 slices, one workgroup each, so that more compute
+    // units share the reads (measured: at 72 rows x 205 splits it gains, at
+    // 512 rows x 61 splits the extra workgroups cost more than they save)
+    const bool sliced = gx * p->batch < 4 * kCUs && lay.plan.max_splits > 64;
+    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, sliced, s) !=
         hipSuccess)
       return TV_ERR_LAUNCH;
   }

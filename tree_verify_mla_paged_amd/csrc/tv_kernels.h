@@ -97,8 +97,9 @@ hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t s
 // ev0 / ev1 (may be null): stamped with the split kernel's own start and end.
 hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent_t ev0,
                         hipEvent_t ev1);
-// many: 1024 threads per row (a single request split many ways), else 256.
-hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
-                        bool many, hipStream_t st);
+// rows: per request (max_q_len * H); sliced: 4 workgroups per row, each
+// merging a quarter of the value dims.
+hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
+                        bool sliced, hipStream_t st);
 
 }  // namespace tv

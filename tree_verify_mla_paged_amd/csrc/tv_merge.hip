@@ -15,37 +15,37 @@
 
 namespace tv {
 
-// One row per workgroup of NT threads (256, or 1024 for rows of many splits),
-// in chunks of up to MERGE_CHUNK splits.  A thread's first U partial-output
-// loads go out before anything else; meanwhile the chunk's split LSEs are read
-// once, cooperatively, and turned into weights in LDS.  Each load is 16 bytes:
-// a thread owns DPT value dims (8 fp16 or 4 fp32), so a split's row takes TPS
-// threads and the workgroup's NPH = NT / TPS phases take alternate splits,
-// combined through LDS at the end: NPH * U splits are in flight at once (64 or
-// 256 with fp16 partials), so a row of a long single request is read in one
-// round trip.  Weights are relative to the running maximum M and are rescaled
-// when a later chunk raises it.
+// One workgroup of 256 threads per (row, slice of VD / DS value dims), in
+// chunks of up to MERGE_CHUNK splits.  DS = 4 spreads the rows of a small
+// problem over four times as many compute units (each reads a quarter of every
+// partial row; the weights are recomputed per slice).  A thread's first U
+// partial-output loads go out before anything else; meanwhile the chunk's
+// split LSEs are read once, cooperatively, and turned into weights in LDS.
+// Each load is 16 bytes: a thread owns DPT value dims (8 fp16 or 4 fp32), so a
+// split's slice takes TPS threads and the workgroup's NPH = 256 / TPS phases
+// take alternate splits, combined through LDS at the end: NPH * U splits are
+// in flight at once.  Weights are relative to the running maximum M and are
+// rescaled when a later chunk raises it.
 constexpr int MERGE_CHUNK = 1024;
 
-// Maximum over the workgroup (NT threads); ends with a barrier.
-template <int NT>
+constexpr int NT = 256;  // threads per workgroup
+
+// Maximum over the workgroup; ends with a barrier.
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = red[0];
-#pragma unroll
-  for (int w = 1; w < NT / 64; ++w) v = fmaxf(v, red[w]);
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   return v;
 }
 
-template <int OUT, bool F16P, int NT>
+template <int OUT, bool F16P, int DS>
 __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   constexpr int U = 16;               // loads per thread in flight
   constexpr int DPT = F16P ? 8 : 4;  // value dims per thread: one 16-byte load
-  constexpr int TPS = VD / DPT;      // threads per split row
+  constexpr int TPS = VD / DS / DPT; // threads per split row slice
   constexpr int NPH = NT / TPS;      // splits in flight across the workgroup
   typedef float accv __attribute__((ext_vector_type(DPT)));
   __shared__ float wgt_s[MERGE_CHUNK];               // w_s
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   const int b = blockIdx.y;
   const int q0 = p.qo_indptr[b];
   const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
-  const int r = blockIdx.x;
+  const int r = blockIdx.x / DS;
+  const int slice = blockIdx.x % DS;
   if (r >= R) return;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
   const int ns = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   const int LS = F16P ? 2 : 1;  // floats per (row, split) in ws_lse
   const float* ls = p.ws_lse + g * p.max_splits * LS;
   const int t = threadIdx.x;
-  const int d = (t % TPS) * DPT;
+  const int d = slice * (VD / DS) + (t % TPS) * DPT;
   const int h = t / TPS;  // phase: splits h, h + NPH, ...
   const float* po = static_cast<const float*>(p.ws_o) + g * p.max_splits * VD + d;
   const _Float16* ph = static_cast<const _Float16*>(p.ws_o) + g * p.max_splits * VD + d;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
       wgt_s[i] = lv;
       m = fmaxf(m, lv);
     }
-    const float Mn = fmaxf(M, block_max<NT>(m, red));
+    const float Mn = fmaxf(M, block_max(m, red));
     if (Mn == -INFINITY) continue;  // every split so far is empty (uniform)
     if (Mn > M) {
       // (w_s and w_s 2^k_s share the factor)
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   }
   if (M != -INFINITY) acc *= 1.f / W;
   const float lse = (M == -INFINITY) ? -INFINITY : M + logf(W);
-  if (t == 0) p.lse[g] = lse;
+  if (t == 0 && slice == 0) p.lse[g] = lse;
 #pragma unroll
   for (int e0 = 0; e0 < DPT; e0 += 4) {
     const f32x4 o4 = f32x4{acc[e0], acc[e0 + 1], acc[e0 + 2], acc[e0 + 3]};
@@ -159,21 +160,21 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   }
 }
 
-hipError_t launch_merge(const MergeParams& p, int grid_x, int batch, int out, bool f16_parts,
-                        bool many, hipStream_t st) {
+hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
+                        bool sliced, hipStream_t st) {
   MergeParams a = p;
   void* args[] = {&a};
-  // [out dtype][fp16 partials][1024 threads]
+  // [out dtype][fp16 partials][4 slices]
   static const void* const fns[2][2][2] = {
-      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 256>),
-        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 1024>)},
-       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 256>),
-        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 1024>)}},
-      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 256>),
-        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 1024>)},
-       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 256>),
-        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 1024>)}}};
-  const void* fn = fns[out == OUT_F32][f16_parts][many];
-  return hipLaunchKernel(fn, dim3(grid_x, batch), dim3(many ? 1024 : 256), args, 0, st);
+      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 1>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, false, 4>)},
+       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 1>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_BF16, true, 4>)}},
+      {{reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 1>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, false, 4>)},
+       {reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 1>),
+        reinterpret_cast<const void*>(&tv_merge_kernel<OUT_F32, true, 4>)}}};
+  const void* fn = fns[out == OUT_F32][f16_parts][sliced];
+  return hipLaunchKernel(fn, dim3(rows * (sliced ? 4 : 1), batch), dim3(NT), args, 0, st);
 }
 }  // namespace tv
