@@ -55,7 +55,7 @@ class TreeVerifyError(RuntimeError):
 import torch  # noqa: E402,F401
 
 if not os.path.exists(LIBRARY_PATH):
-    raise ImportError("libtreeverify.so is not built: run `python -m tree_verify_mla_paged_amd.build` "
+    raise ImportError("libtreeverify.so is not built: run `python tree_verify_mla_paged_amd/build.py` "
                       "(hipcc, gfx950) before using the GPU path")
 
 _lib = ctypes.CDLL(LIBRARY_PATH)
