@@ -202,6 +202,40 @@ def write_traffic(args):
     print(json.dumps(d["workloads"][key], indent=1))
 
 
+SCRUB_BYTES = 1 << 30  # larger than the 256 MB MALL plus every XCD's L2
+
+
+def cold_cache_times(call, stream, n):
+    """Whole-call time with cold caches: before each call a 1 GiB fill kernel
+    evicts the pool, the indices and the mask from the MALL and the L2s.  The
+    events bracket the call only, on its own stream.  The same bracketing of
+    back-to-back calls without the fill gives the warm figure measured the
+    same way (event handling adds a few microseconds to each)."""
+    import torch
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+
+    def timed(with_scrub):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        with torch.cuda.stream(stream):
+            for i in range(n):
+                if with_scrub:
+                    scrub.fill_(i & 0xFF)
+                evs[i][0].record(stream)
+                call()
+                evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+                "p90_us": float(np.percentile(us, 90))}
+
+    timed(True)  # first pass: allocator and fill kernel warm-up
+    res = {"calls": n, "scrub_bytes": SCRUB_BYTES, "cold": timed(True), "warm": timed(False)}
+    del scrub
+    torch.cuda.synchronize()
+    return res
+
+
 def cpu_baseline(w, gpu_out, gpu_lse, kv_bytes, budget_s, out_f32):
     """Time the fp64 oracle on a bounded sample of rows and scale to the call."""
     import oracle
@@ -256,6 +290,8 @@ def main():
     ap.add_argument("--precise", action="store_true",
                     help="probabilities as a bf16 hi + lo pair in the P.V product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=30,
+                    help="calls timed with a cache scrub before each (0 = skip)")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--counter-workload", type=int, default=0, metavar="N",
                     help="run the calibration copy and N calls for rocprofv3 --pmc, no timing")
@@ -349,6 +385,8 @@ def main():
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
 
+    cold = cold_cache_times(call, stream, args.cold_calls) if args.cold_calls > 0 else None
+
     kv_bytes, total_bytes, flops = algorithmic(w)
     us_per_call = ms_per_step * 1e3
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -376,6 +414,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, bf16-rounded N(0,1))",
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "graph_us_per_call": graph_us,
+        "cold_cache": cold,
         "floor_fraction": max(t_hbm, t_mfma) / (ms_per_step * 1e-3),
         "config": {"workload": desc, "requests": w.batch, "n_draft": int(w.max_q_len),
                    "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,
