@@ -77,7 +77,17 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def workload(cfg: str, poison: bool):
+def workload(cfg: str, poison: bool, prefix_visible: bool = False):
+    w, desc, splits = _workload(cfg, poison)
+    if prefix_visible:
+        w = W.prefix_visible_form(w)
+        desc += "; mask in the prefix-visible form (draft keys only)"
+    return w, desc, splits
+
+
+def _workload(cfg: str, poison: bool):
+    if cfg in W.EXTRA_DESC:
+        return W.extra(cfg, poison=poison), W.EXTRA_DESC[cfg], None
     if cfg.startswith("S"):
         k = int(cfg[1:])
         w = W.sweep(k, poison=poison)
@@ -133,7 +143,7 @@ def counter_workload(args):
     for _ in range(3):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    w, _, cfg_splits = workload(args.config, poison=False)
+    w, _, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
     splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in dict(
         q=w.q.view(np.int16), kv=w.kv.view(np.int16), kv_indices=w.kv_indices,
@@ -142,7 +152,8 @@ def counter_workload(args):
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
                         tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
-                        tv.FLAG_PRECISE_P if args.precise else 0)
+                        (tv.FLAG_PRECISE_P if args.precise else 0) |
+                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
     out = torch.empty((w.total_q, w.num_heads, 512),
                       dtype=torch.float32 if args.out_f32 else torch.bfloat16, device="cuda")
     lse = torch.empty((w.total_q, w.num_heads), dtype=torch.float32, device="cuda")
@@ -282,7 +293,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="3", help="1-5 (benchmark configurations) or S1-S3")
+    ap.add_argument("--config", default="3",
+                    help="1-5 (benchmark configurations), S1-S3 (long-prefix sweep), "
+                         "D (plain decode) or K (chain verify)")
+    ap.add_argument("--prefix-visible", action="store_true",
+                    help="pass the mask in the prefix-visible form (draft keys only)")
     ap.add_argument("--splits", type=int, default=0,
                     help="KV split count (0 = the library's plan; -1 = the configuration's own "
                          "split count if it names one)")
@@ -315,7 +330,7 @@ def main():
     import torch
     import tree_verify_mla_paged_amd as tv
 
-    w, desc, cfg_splits = workload(args.config, poison=False)
+    w, desc, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
     splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
     dev = "cuda"
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in dict(
@@ -325,7 +340,8 @@ def main():
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
                         tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
-                        tv.FLAG_PRECISE_P if args.precise else 0)
+                        (tv.FLAG_PRECISE_P if args.precise else 0) |
+                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
     plan = tv.plan(p)
     N, H = w.total_q, w.num_heads
     out = torch.empty((N, H, 512), dtype=torch.float32 if args.out_f32 else torch.bfloat16,
@@ -400,7 +416,9 @@ def main():
         achieved = total_bytes / (split_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-    roof["traffic"] = measured_traffic(args.config, splits, bool(args.precise))
+    # the counter summary covers the full mask form only
+    roof["traffic"] = (None if args.prefix_visible else
+                       measured_traffic(args.config, splits, bool(args.precise)))
     roof["kernel"] = "tv_split_kernel"
     roof["kernel_avg_us"] = split_avg_ms * 1e3
     roof["kernel_timed_launches"] = len(split_ms)
@@ -419,7 +437,7 @@ def main():
         "config": {"workload": desc, "requests": w.batch, "n_draft": int(w.max_q_len),
                    "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,
                    "plan": plan, "out_dtype": "f32" if args.out_f32 else "bf16",
-                   "precise_p": bool(args.precise),
+                   "precise_p": bool(args.precise), "prefix_visible": bool(args.prefix_visible),
                    "gathered_kv_bytes": kv_bytes, "visible_pairs_x_heads": w.visible_pairs() * H},
         "roofline": roof,
     }

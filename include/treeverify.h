@@ -68,6 +68,16 @@ typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
  * Meant for value distributions with large outliers. */
 #define TV_FLAG_PRECISE_P 1
 
+/* tv_problem.flags.  The mask covers the draft keys only: every draft row sees
+ * all P_b = L_b - n_b prefix keys of its request, and the mask block of request
+ * b is n_b x n_b bytes, row stride n_b, where byte i * n_b + k says whether draft
+ * i sees draft k's key (key P_b + k).  This is the prefix-visible form of the
+ * custom mask that the pages name as the integration's other option (page 3,
+ * "The Pivot to Live Cutover", section "The Technical Investigation"); it spares
+ * the caller the n_b x L_b block, which at a 200k prefix is n_b x 200k bytes.
+ * The results equal those of the full mask with every prefix byte nonzero. */
+#define TV_FLAG_PREFIX_VISIBLE 2
+
 /* Host-side description of one call.  Device-side lengths may vary between
  * calls (or graph replays) as long as they stay within these bounds. */
 typedef struct tv_problem {
@@ -106,8 +116,8 @@ tv_status tv_get_plan(const tv_problem* p, tv_plan* plan);
  * bytes:
  *  - one 32-bit visibility word per (draft token, 32-key tile), only when some
  *    32 consecutive rows (draft * H + head, from a multiple of 32) span more
- *    than 4 draft tokens (H < 8, H = 9); otherwise the kernels read the mask
- *    bytes directly;
+ *    than 4 draft tokens (H < 8, H = 9), or with TV_FLAG_PREFIX_VISIBLE;
+ *    otherwise the kernels read the mask bytes directly;
  *  - when more than one split is used, the per-split partial outputs:
  *    total_q * H * max_splits entries of 512 fp16 values plus two fp32 (lse,
  *    scale exponent), or with TV_FLAG_PRECISE_P of 512 + 1 fp32;
@@ -127,6 +137,7 @@ size_t tv_workspace_bytes(const tv_problem* p);
  *               qo_indptr[b] .. qo_indptr[b+1]-1
  *   mask        uint8 [total_mask], nonzero = visible
  *   mask_indptr int32 [B+1]; mask_indptr[b+1] - mask_indptr[b] = n_b * L_b
+ *               (n_b * n_b with TV_FLAG_PREFIX_VISIBLE)
  *   sm_scale    score scale (e.g. 1/sqrt(192)); positive and finite, else
  *               TV_ERR_SHAPE
  *   out         [total_q, H, 512] bf16 (round to nearest even) or fp32
@@ -173,7 +184,8 @@ tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* k
  * TV_ERR_HIP if a copy fails, or the host-side errors of tv_verify_attn.  Checks:
  * indptrs non-decreasing and within total_q / total_kv / total_mask; every
  * n_b <= max_q_len and L_b <= max_kv_len; L_b >= n_b; the mask block of
- * request b is exactly n_b * L_b bytes; every slot in [0, num_slots).  The last
+ * request b is exactly n_b * L_b bytes (n_b * n_b with TV_FLAG_PREFIX_VISIBLE);
+ * every slot in [0, num_slots).  The last
  * two catch both halves of the marshaling mistake the pages describe (page 2,
  * section "The Long Road to Parity"): draft slots missing from kv_indices, and
  * a mask laid out with the prefix-only row stride.  Mask contents are not read.

@@ -18,6 +18,11 @@
  *    in the same section; the per-sequence mask_indptr indexing of page 3,
  *    "The Pivot to Live Cutover", section "The Technical Investigation").
  *    The same mask row serves all H heads of draft token i.
+ *  - Prefix-visible form (the custom mask without its prefix part, page 3,
+ *    section "The Technical Investigation"): every draft row sees all
+ *    P_b = L_b - n_b prefix keys, and the block of request b holds only the
+ *    draft keys, n_b x n_b bytes with row stride n_b: byte i * n_b + k says
+ *    whether row i sees key P_b + k.
  *  - Absorbed MLA: a query row and a key row have 576 dims (512 latent + 64
  *    RoPE, page 3, section "Input Knowledge Required"); the score uses all
  *    576, the value is the first 512 dims of the same key row.
@@ -66,7 +71,7 @@ int tvo_check(const tvo_args* a) {
     int64_t n = q1 - q0, L = k1 - k0;
     /* draft slots are part of kv_indices, so every draft row has its own key */
     if (L < n) return TVO_ERR_KVLEN;
-    if (m1 - m0 != n * L) return TVO_ERR_MASKLEN;
+    if (m1 - m0 != n * (a->prefix_visible ? n : L)) return TVO_ERR_MASKLEN;
     for (int64_t j = k0; j < k1; ++j)
       if (a->kv_indices[j] < 0 || a->kv_indices[j] >= a->num_slots) return TVO_ERR_SLOT;
   }
@@ -95,7 +100,9 @@ static void one_row(const tvo_args* a, int64_t t, int32_t h, double* o, double* 
   const int64_t i = t - a->qo_indptr[b];
   const int64_t k0 = a->kv_indptr[b];
   const int64_t L = a->kv_indptr[b + 1] - k0;
-  const uint8_t* mrow = a->mask + a->mask_indptr[b] + i * L;
+  const int64_t n = a->qo_indptr[b + 1] - a->qo_indptr[b];
+  const int64_t P = a->prefix_visible ? L - n : 0; /* keys visible without a mask byte */
+  const uint8_t* mrow = a->mask + a->mask_indptr[b] + i * (a->prefix_visible ? n : L);
   const uint16_t* qrow = a->q + ((size_t)t * a->num_heads + h) * QK;
   const double c = (double)a->sm_scale; /* the fp32 scale, widened exactly */
 
@@ -105,7 +112,7 @@ static void one_row(const tvo_args* a, int64_t t, int32_t h, double* o, double* 
   /* visible set, ascending key order */
   int64_t nv = 0;
   for (int64_t j = 0; j < L; ++j)
-    if (mrow[j] != 0) jbuf[nv++] = j;
+    if (j < P || mrow[j - P] != 0) jbuf[nv++] = j;
   if (nv == 0) return;
 
   /* pass 1: scaled scores over all 576 dims, and their maximum */

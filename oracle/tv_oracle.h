@@ -13,7 +13,8 @@ enum {
   TVO_ERR_SHAPE = -2,
   TVO_ERR_INDPTR = -3,   /* an indptr is negative, decreasing or past its buffer */
   TVO_ERR_KVLEN = -4,    /* L_b < n_b: draft slots missing from kv_indices      */
-  TVO_ERR_MASKLEN = -5,  /* mask block of request b is not n_b * L_b bytes       */
+  TVO_ERR_MASKLEN = -5,  /* mask block of request b is not n_b * L_b bytes
+                            (n_b * n_b in the prefix-visible form)               */
   TVO_ERR_SLOT = -6,     /* a kv_indices entry is outside [0, num_slots)         */
   TVO_ERR_ALLOC = -7
 };
@@ -33,6 +34,9 @@ typedef struct {
   int64_t total_kv;
   int64_t total_mask;
   float sm_scale;
+  int32_t prefix_visible;      /* 0: block b is n_b x L_b bytes, stride L_b.
+                                  1: block b is n_b x n_b bytes (the draft keys,
+                                  stride n_b) and every prefix key is visible  */
 } tvo_args;
 
 /* Validate every precondition; TVO_OK or the first violation found. */

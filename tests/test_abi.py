@@ -122,7 +122,7 @@ def test_bad_shapes_are_rejected():
         with pytest.raises(tv.TreeVerifyError) as e:
             tv.plan(prob(**kw))
         assert e.value.code == 2
-    for kw in [dict(out_dtype=7), dict(flags=2), dict(flags=-1)]:
+    for kw in [dict(out_dtype=7), dict(flags=4), dict(flags=-1)]:
         with pytest.raises(tv.TreeVerifyError) as e:
             tv.plan(prob(**kw))
         assert e.value.code == 4
@@ -140,6 +140,21 @@ def test_bad_shapes_are_rejected():
     assert tv.plan(prob(**many))["merge"]
     assert tv.workspace_bytes(prob(flags=tv.FLAG_PRECISE_P, **many)) > \
         tv.workspace_bytes(prob(**many))
+
+
+def test_prefix_visible_flag_packs_words():
+    """The prefix-visible mask form goes through the packed visibility words,
+    also where the full form reads the mask bytes directly (16 heads), and keeps
+    the split plan."""
+    base = dict(num_heads=16, max_kv_len=40000, total_kv=40000)
+    full, pv = prob(**base), prob(flags=tv.FLAG_PREFIX_VISIBLE, **base)
+    pf, pp = tv.plan(full), tv.plan(pv)
+    assert {k: v for k, v in pf.items() if k != "workspace_bytes"} == \
+        {k: v for k, v in pp.items() if k != "workspace_bytes"}
+    words = full.total_q * ((40000 + 31) // 32) * 4
+    assert pp["workspace_bytes"] - pf["workspace_bytes"] == (words + 255) // 256 * 256
+    both = prob(flags=tv.FLAG_PREFIX_VISIBLE | tv.FLAG_PRECISE_P, **base)
+    assert tv.plan(both)["max_splits"] == pf["max_splits"]
 
 
 def test_null_pointers_and_short_workspace_fail_before_any_launch():

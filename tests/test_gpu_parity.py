@@ -355,3 +355,86 @@ def test_check_inputs_catches_the_marshaling_bug():
     bad = t["kv_indices"].clone()
     bad[3] = w.num_slots
     assert tv.check_inputs(p, bad, t["kv_indptr"], t["qo_indptr"], t["mask_indptr"]) == (5, 0)
+
+
+# ---------------------------------------------- prefix-visible mask form
+
+PV_SHAPES = [
+    # seed, prefix lengths, draft counts, heads, num_splits
+    (301, [100], [5], 8, 0),
+    (302, [250], [20], 16, 2),        # 16 heads: the full form reads bytes, this one words
+    (303, [300, 7, 0, 95], [3, 2, 0, 6], 5, 4),
+    (304, [1000], [9], 8, 7),
+    (305, [0], [4], 3, 0),            # no prefix: the block is the whole mask
+]
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H,ns", PV_SHAPES)
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_prefix_visible_small(seed, prefix, ndraft, H, ns, out_f32):
+    print("prefix-visible seed=%d H=%d ns=%d f32=%s" % (seed, H, ns, out_f32), flush=True)
+    w = W.prefix_visible_form(W.small(seed, prefix, ndraft, num_heads=H))
+    full_check(w, num_splits=ns, out_f32=out_f32, label="pv%d" % seed)
+
+
+def test_prefix_visible_arbitrary_draft_block():
+    """Random draft-key bits; a row of a request without prefix sees nothing."""
+    w = W.prefix_visible_form(W.small(306, [70, 0], [6, 3], num_heads=4))
+    rng = np.random.default_rng(306)
+    w.mask[:] = (rng.random(w.mask.size) < 0.4).astype(np.uint8)
+    w.mask[w.mask_indptr[1]:w.mask_indptr[1] + 3] = 0
+    for ns in (1, 3):
+        print("prefix-visible random block ns=%d" % ns, flush=True)
+        full_check(w, num_splits=ns, out_f32=True, label="pv random ns=%d" % ns)
+
+
+def test_prefix_visible_equals_full_mask_bits():
+    """A tree mask and its prefix-visible form give the kernels the same
+    visibility, so the outputs agree bit for bit."""
+    for w in (W.small(307, [700], [12], num_heads=16), W.config(2)):
+        print("prefix-visible vs full: %s" % w.name, flush=True)
+        a = GpuCall(w, out_f32=True)
+        a.call()
+        b = GpuCall(W.prefix_visible_form(w), out_f32=True)
+        b.call()
+        assert np.array_equal(a.out_bits(), b.out_bits())
+        assert np.array_equal(a.lse.cpu().numpy().view(np.int32),
+                              b.lse.cpu().numpy().view(np.int32))
+
+
+def test_prefix_visible_c3():
+    print("C3 prefix-visible", flush=True)
+    sampled_check(W.prefix_visible_form(W.config(3)), 96, label="C3 prefix-visible")
+
+
+def test_check_inputs_prefix_visible_stride():
+    w = W.prefix_visible_form(W.config(1))
+    t = upload(w)
+    p = tv.make_problem(1, 8, 9, 9, 30, w.num_slots, 30, 81, flags=tv.FLAG_PREFIX_VISIBLE)
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                           t["mask_indptr"]) == (0, -1)
+    # the full n x L block (270 bytes) announced as prefix-visible
+    full = W.config(1)
+    p = tv.make_problem(1, 8, 9, 9, 30, w.num_slots, 30, 270, flags=tv.FLAG_PREFIX_VISIBLE)
+    mp = torch.from_numpy(full.mask_indptr).to("cuda")
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"], mp) == (5, 0)
+
+
+# ------------------------------ other workloads of the same kernels
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_plain_decode_batch(H):
+    """One query token per request (mask: the prefix and itself): plain MLA
+    decode over the paged pool."""
+    print("plain decode H=%d" % H, flush=True)
+    w = W.chain(401, [5000, 32768, 100, 1], 1, num_heads=H)
+    full_check(w, out_f32=True, label="decode H=%d" % H)
+
+
+@pytest.mark.parametrize("ns", [0, 3])
+def test_causal_chain_verify(ns):
+    """Drafts forming one chain: a causal mask over the draft keys."""
+    print("chain verify ns=%d" % ns, flush=True)
+    w = W.chain(402, [3000, 17], 12, num_heads=16)
+    full_check(w, num_splits=ns, out_f32=True, label="chain ns=%d" % ns)
+    full_check(W.prefix_visible_form(w), num_splits=ns, label="chain pv ns=%d" % ns)

@@ -407,3 +407,90 @@ def test_generated_configs_structure():
             assert np.all(m[:, :P] == 1)
             assert np.all(np.diag(m[:, P:]) == 1)          # each draft sees itself
             assert np.all(np.triu(m[:, P:], 1) == 0)        # never a later draft
+
+
+# ------------------------------------------- prefix-visible form of the mask
+
+def brute_prefix_visible(w):
+    """Scalar loops over the prefix-visible form, read straight from its
+    definition: row i of request b sees key j iff j < P_b = L_b - n_b, or
+    byte i * n_b + (j - P_b) of the request's n_b x n_b block is nonzero."""
+    N, H = w.q.shape[0], w.num_heads
+    out = np.zeros((N, H, 512))
+    lse = np.full((N, H), -np.inf)
+    c = float(w.sm_scale)
+    for b in range(w.batch):
+        n = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
+        L = int(w.kv_indptr[b + 1] - w.kv_indptr[b])
+        P = L - n
+        for i in range(n):
+            t = int(w.qo_indptr[b]) + i
+            vis = [j for j in range(L)
+                   if j < P or w.mask[int(w.mask_indptr[b]) + i * n + (j - P)]]
+            for h in range(H):
+                if not vis:
+                    continue
+                qv = [float(x) for x in f64(w.q[t, h])]
+                ks = [[float(x) for x in f64(w.kv[w.kv_indices[int(w.kv_indptr[b]) + j]])]
+                      for j in vis]
+                e = [math.exp(c * math.fsum(a * bb for a, bb in zip(qv, k))) for k in ks]
+                z = math.fsum(e)
+                for d in range(512):
+                    out[t, h, d] = math.fsum(e[v] * ks[v][d] for v in range(len(vis))) / z
+                lse[t, h] = math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H", [(31, [100], [5], 4), (32, [300, 7, 0, 95],
+                                                                        [3, 2, 0, 6], 3),
+                                                   (33, [0], [4], 2)])
+def test_prefix_visible_form_equals_full_mask(seed, prefix, ndraft, H):
+    """A tree mask sees its whole prefix, so its prefix-visible form (the draft
+    columns only) selects the same keys in the same order: bit-identical."""
+    w = W.small(seed, prefix, ndraft, num_heads=H)
+    pv = W.prefix_visible_form(w)
+    assert pv.mask.size == sum(n * n for n in ndraft)
+    a, la = oracle.run(w)
+    b, lb = oracle.run(pv)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_prefix_visible_brute_force_with_arbitrary_draft_block():
+    """Random (not tree) draft-key bits, some rows seeing no draft key at all."""
+    w = W.prefix_visible_form(W.small(34, [3, 0], [3, 2], num_heads=2))
+    rng = np.random.default_rng(34)
+    w.mask[:] = (rng.random(w.mask.size) < 0.5).astype(np.uint8)
+    w.mask[0:3] = 0  # request 0, draft 0 sees only its 3 prefix keys
+    o, l = oracle.run(w)
+    bo, bl = brute_prefix_visible(w)
+    assert np.allclose(o, bo, rtol=1e-13, atol=1e-15)
+    fin = np.isfinite(bl)
+    assert np.array_equal(fin, np.isfinite(l))
+    assert np.allclose(l[fin], bl[fin], rtol=1e-13, atol=1e-13)
+    # request 1 has no prefix: a row whose draft bits are all 0 sees nothing
+    w.mask[w.mask_indptr[1]:w.mask_indptr[1] + 2] = 0
+    o, l = oracle.run(w)
+    t = int(w.qo_indptr[1])
+    assert np.all(o[t] == 0) and np.all(np.isneginf(l[t]))
+
+
+def test_prefix_visible_stride_is_checked():
+    """Mixing the two forms is the marshaling mistake again: a full n x L block
+    passed as prefix-visible (or the reverse) is rejected."""
+    w = W.small(35, [40], [4], num_heads=1)
+    pv = W.prefix_visible_form(w)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.attention(w.q, w.kv, w.kv_indices, w.kv_indptr, w.qo_indptr, w.mask,
+                         w.mask_indptr, w.sm_scale, w.num_heads, prefix_visible=True)
+    assert e.value.code == -5
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.attention(pv.q, pv.kv, pv.kv_indices, pv.kv_indptr, pv.qo_indptr, pv.mask,
+                         pv.mask_indptr, pv.sm_scale, pv.num_heads, prefix_visible=False)
+    assert e.value.code == -5
+
+
+def test_prefix_visible_form_needs_a_visible_prefix():
+    w = W.small(36, [10], [3], num_heads=1)
+    w.mask[0] = 0
+    with pytest.raises(ValueError):
+        W.prefix_visible_form(w)

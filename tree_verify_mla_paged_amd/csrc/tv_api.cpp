@@ -73,7 +73,8 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL)
     return TV_ERR_SHAPE;
   if (p->out_dtype != TV_OUT_BF16 && p->out_dtype != TV_OUT_F32) return TV_ERR_UNSUPPORTED;
-  if ((p->flags & ~TV_FLAG_PRECISE_P) != 0 || p->reserved != 0) return TV_ERR_UNSUPPORTED;
+  if ((p->flags & ~(TV_FLAG_PRECISE_P | TV_FLAG_PREFIX_VISIBLE)) != 0 || p->reserved != 0)
+    return TV_ERR_UNSUPPORTED;
   if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
   // per-request key offsets are 32-bit byte offsets (4 * key) in the kernels
   if (p->max_kv_len >= (1 << 30)) return TV_ERR_SHAPE;
@@ -108,7 +109,10 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   lay->grid = ceil_div(total_work, 8 * lay->xcd_group) * 8 * lay->xcd_group;
 
   lay->max_tiles = (int32_t)std::max<int64_t>(1, ceil_div(L, tv::TILE_KEYS));
-  lay->mask_bytes = waves_span_few_drafts(rows_max, p->num_heads);
+  // the prefix-visible form always goes through the packed words: the pack
+  // kernel expands it, the split kernel sees the same words either way
+  lay->mask_bytes = (p->flags & TV_FLAG_PREFIX_VISIBLE) == 0 &&
+                    waves_span_few_drafts(rows_max, p->num_heads);
   lay->words_off = 0;
   lay->words_bytes = lay->mask_bytes ? 0 : align256(p->total_q * lay->max_tiles * 4);
   int64_t off = lay->words_bytes;
@@ -187,6 +191,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     pp.split_keys = lay.plan.split_keys;
     pp.num_heads = p->num_heads;
     pp.batch = p->batch;
+    pp.prefix_visible = (p->flags & TV_FLAG_PREFIX_VISIBLE) ? 1 : 0;
     // a wave per draft row and 512 keys (tv_pack_mask_kernel), 4 waves per workgroup
     const int64_t gx =
         lay.mask_bytes
@@ -302,6 +307,7 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
   if (!kv_indptr || !qo_indptr || !mask_indptr) return TV_ERR_NULL;
   if (p->total_kv > 0 && !kv_indices) return TV_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool prefix_visible = (p->flags & TV_FLAG_PREFIX_VISIBLE) != 0;
   const size_t nb = (size_t)p->batch + 1;
   std::vector<int32_t> kvp(nb), qop(nb), mp(nb), idx((size_t)p->total_kv);
   if (hipMemcpyAsync(kvp.data(), kv_indptr, nb * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -319,7 +325,8 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
                      q1 > p->total_q || k1 > p->total_kv || m1 > p->total_mask ||
                      q1 - q0 > p->max_q_len || k1 - k0 > p->max_kv_len ||
                      k1 - k0 < q1 - q0 ||               // draft slots missing from kv_indices
-                     m1 - m0 != (q1 - q0) * (k1 - k0);  // mask stride is not L_b
+                     // mask stride is not L_b (n_b in the prefix-visible form)
+                     m1 - m0 != (q1 - q0) * (prefix_visible ? q1 - q0 : k1 - k0);
     if (bad) {
       if (bad_request) *bad_request = b;
       return TV_ERR_INPUT;
@@ -340,7 +347,7 @@ const char* tv_status_str(tv_status s) {
     case TV_ERR_NULL: return "a required pointer is NULL";
     case TV_ERR_SHAPE: return "a size in tv_problem is out of range or inconsistent";
     case TV_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
-    case TV_ERR_UNSUPPORTED: return "unsupported output dtype";
+    case TV_ERR_UNSUPPORTED: return "unsupported output dtype or flag, or reserved != 0";
     case TV_ERR_INPUT: return "device-side input violates a precondition";
     case TV_ERR_LAUNCH: return "kernel launch failed (the library holds gfx950 code only)";
     case TV_ERR_HIP: return "HIP runtime call failed";

@@ -41,6 +41,9 @@ struct PackParams {
   int32_t sched_block;        // blockIdx.x of the workgroup that writes `order` (-1: none)
   int32_t* order;             // [total_work]: work item at dispatch position p, or -1
   int32_t total_work, max_splits, row_blocks, split_keys, num_heads, batch;
+  // 1: the mask block of request b is n_b x n_b (draft keys only) and every
+  // draft sees all L_b - n_b prefix keys
+  int32_t prefix_visible;
 };
 
 struct SplitScalars {

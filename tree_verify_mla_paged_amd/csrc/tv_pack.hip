@@ -15,10 +15,11 @@
 namespace tv {
 
 // Word (token qo_indptr[b] + i, tile) bit k = mask byte of key 32*tile + k of draft i;
-// keys at or past L_b give 0.  One wave per PACK_SEGS * 64 keys of a draft row:
-// lane l reads key 64j + l of each 64-key segment j (one coalesced 64-byte load
-// per segment), and the segment's ballot is its two words; lanes 0..2*PACK_SEGS-1
-// then store one word each.
+// keys at or past L_b give 0.  In the prefix-visible form the block holds the
+// draft keys only (n_b x n_b bytes) and the bits of the prefix keys are 1.  One
+// wave per PACK_SEGS * 64 keys of a draft row: lane l reads key 64j + l of each
+// 64-key segment j (one coalesced 64-byte load per segment), and the segment's
+// ballot is its two words; lanes 0..2*PACK_SEGS-1 then store one word each.
 constexpr int PACK_SEGS = PACK_KEYS / 64;
 
 // Longest-first dispatch order of the split kernel's work items, by one
@@ -106,13 +107,25 @@ __global__ __launch_bounds__(256) void tv_pack_mask_kernel(PackParams p) {
   const int i = unit / chunks;
   const int c = unit - i * chunks;
   const int lane = threadIdx.x & 63;
-  const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * L;
   const int k0 = c * 64 * PACK_SEGS + lane;
   uint8_t v[PACK_SEGS];
+  if (p.prefix_visible) {
+    // draft keys only: key k >= P of draft i is byte i * n + (k - P) of the
+    // block; every prefix key is visible (L >= n is a precondition)
+    const int P = L - n;
+    const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * n;
 #pragma unroll
-  for (int j = 0; j < PACK_SEGS; ++j) {
-    const int k = k0 + 64 * j;
-    v[j] = k < L ? m[k] : 0;
+    for (int j = 0; j < PACK_SEGS; ++j) {
+      const int k = k0 + 64 * j;
+      v[j] = k >= L ? 0 : (k < P ? 1 : m[k - P]);
+    }
+  } else {
+    const uint8_t* m = p.mask + p.mask_indptr[b] + (int64_t)i * L;
+#pragma unroll
+    for (int j = 0; j < PACK_SEGS; ++j) {
+      const int k = k0 + 64 * j;
+      v[j] = k < L ? m[k] : 0;
+    }
   }
   uint32_t mine = 0;
 #pragma unroll

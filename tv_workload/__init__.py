@@ -127,6 +127,9 @@ class Workload:
     prefix_lens: list = dataclasses.field(default_factory=list)
     parents: list = dataclasses.field(default_factory=list)
     name: str = ""
+    # mask in the prefix-visible form: n_b x n_b bytes per request (draft keys
+    # only), every prefix key visible
+    prefix_visible: bool = False
 
     @property
     def batch(self) -> int:
@@ -161,8 +164,11 @@ class Workload:
         return int(self.kv_lens.sum()) * QK_DIM * 2
 
     def visible_pairs(self) -> int:
-        """(draft row, key) pairs whose mask byte is nonzero, summed over requests."""
-        return int(np.count_nonzero(self.mask[self.mask_indptr[0]:self.mask_indptr[-1]]))
+        """Visible (draft row, key) pairs, summed over requests."""
+        nz = int(np.count_nonzero(self.mask[self.mask_indptr[0]:self.mask_indptr[-1]]))
+        if self.prefix_visible:
+            nz += int((self.q_lens * (self.kv_lens - self.q_lens)).sum())
+        return nz
 
 
 def _spawn(seed: int):
@@ -289,3 +295,52 @@ def small(seed: int, prefix_lens: Sequence[int], n_drafts: Sequence[int], num_he
     pool = pool if pool is not None else max(64, 2 * need)
     return build(seed, prefix_lens, parents, num_heads, pool, outlier_p=outlier_p, poison=poison,
                  name="small%d" % seed)
+
+
+def prefix_visible_form(w: Workload) -> Workload:
+    """The same workload with its mask in the prefix-visible form: per request
+    only the draft-key columns (the last n_b of each row), n_b x n_b bytes,
+    row stride n_b.  The prefix columns must all be visible (true of tree
+    masks); the visible sets are unchanged."""
+    blocks = []
+    for b in range(w.batch):
+        n, L = int(w.q_lens[b]), int(w.kv_lens[b])
+        m = w.mask[w.mask_indptr[b]:w.mask_indptr[b + 1]].reshape(n, L)
+        if not np.all(m[:, :L - n] != 0):
+            raise ValueError("request %d: a prefix key is masked; no prefix-visible form" % b)
+        blocks.append(np.ascontiguousarray(m[:, L - n:]).reshape(-1))
+    mask_indptr = np.zeros(w.batch + 1, dtype=np.int64)
+    mask_indptr[1:] = np.cumsum([x.size for x in blocks])
+    mask = np.concatenate(blocks) if blocks else np.zeros(0, np.uint8)
+    return dataclasses.replace(w, mask=mask.astype(np.uint8),
+                               mask_indptr=mask_indptr.astype(np.int32), prefix_visible=True,
+                               name=w.name + "/prefix-visible")
+
+
+def chain(seed: int, prefix_lens: Sequence[int], n: int, num_heads: int,
+          pool: Optional[int] = None, poison: bool = True, name: str = "") -> Workload:
+    """Requests whose n draft tokens form one chain (draft i's parent is i - 1):
+    a causal mask over the drafts.  n = 1 is plain decode: one query token per
+    request seeing its prefix and itself."""
+    parents = [np.arange(-1, n - 1, dtype=np.int32) for _ in prefix_lens]
+    need = int(sum(prefix_lens)) + n * len(prefix_lens)
+    pool = pool if pool is not None else max(64, 2 * need)
+    return build(seed, prefix_lens, parents, num_heads, pool, poison=poison,
+                 name=name or "chain%d" % seed)
+
+
+# Workloads of the same kernels beyond tree verification (not part of the five
+# configurations): plain MLA decode with all 128 heads of a model on one GPU,
+# and a causal chain of drafts.
+EXTRA_DESC = {
+    "D": "D: plain decode, 8 requests x 1 token, prefix 32768, H=128, pool 524288",
+    "K": "K: chain verify, 1 request, 16 drafts in a chain, prefix 32768, H=16, pool 200000",
+}
+
+
+def extra(key: str, poison: bool = True) -> Workload:
+    if key == "D":
+        return chain(301, [32768] * 8, 1, 128, pool=524288, poison=poison, name="D")
+    if key == "K":
+        return chain(302, [32768], 16, 16, pool=200000, poison=poison, name="K")
+    raise ValueError("unknown workload %r" % key)
