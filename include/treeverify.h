@@ -194,6 +194,72 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
                           const int32_t* kv_indptr, const int32_t* qo_indptr,
                           const int32_t* mask_indptr, void* stream, int32_t* bad_request);
 
+/*
+ * The marshaling step before tv_verify_attn, on the device (page 2 "Flipping
+ * the Switch", section "The Long Road to Parity": the draft tokens' latent rows
+ * are written into the pool at their slots, and those slots follow the prefix
+ * slots in kv_indices; leaving them out was the pages' parity failure).  For
+ * request b with P_b = prefix_indptr[b+1] - prefix_indptr[b] prefix keys and
+ * n_b = qo_indptr[b+1] - qo_indptr[b] draft tokens:
+ *
+ *   kv_buf[out_cache_loc[t]] = draft_kv[t]        for every draft token t
+ *   kv_indptr[b]   = prefix_indptr[b] + qo_indptr[b]   (so L_b = P_b + n_b)
+ *   kv_indices[kv_indptr[b] + j] = prefix_indices[prefix_indptr[b] + j]  (j < P_b)
+ *                                = out_cache_loc[qo_indptr[b] + j - P_b] (j >= P_b)
+ *   mask_indptr[b] = sum over requests before b of n * L (n * n with
+ *                    TV_FLAG_PREFIX_VISIBLE)
+ *   mask row i of request b: every prefix key visible; draft key k (column
+ *                    P_b + k, or k in the prefix-visible form) visible iff k
+ *                    is i or an ancestor of i in the draft tree
+ *
+ * The tree is given as parents[t] for every draft token t: the request-local
+ * index of its parent, -1 for a root, and smaller than the token's own index
+ * (parents precede children).  The outputs are exactly the inputs
+ * tv_verify_attn takes.  Capture-safe: two kernel launches on `stream`.
+ */
+typedef struct tv_append_problem {
+  int32_t batch;        /* B >= 0                                                    */
+  int32_t max_q_len;    /* >= every n_b                                             */
+  int32_t max_kv_len;   /* >= every P_b + n_b                                       */
+  int32_t flags;        /* TV_FLAG_PREFIX_VISIBLE or 0; other bits TV_ERR_UNSUPPORTED */
+  int64_t total_q;      /* rows of draft_kv, out_cache_loc, parents; >= qo_indptr[B]  */
+  int64_t num_slots;    /* rows of kv_buf                                           */
+  int64_t total_prefix; /* entries of prefix_indices                                */
+  int64_t total_kv;     /* capacity of kv_indices (>= prefix_indptr[B] + qo_indptr[B]),
+                           < 2^31                                                    */
+  int64_t total_mask;   /* capacity of mask in bytes, < 2^31                         */
+} tv_append_problem;
+
+/*
+ *   draft_kv       bf16 [total_q, 576], 16-byte aligned; NULL: the pool is not
+ *                  written (the rows are already there) and kv_buf may be NULL
+ *   out_cache_loc  int32 [total_q]: pool slot of each draft token
+ *   prefix_indices int32 [total_prefix]; prefix_indptr int32 [B+1]
+ *   qo_indptr      int32 [B+1]
+ *   parents        int32 [total_q], or NULL: no mask bytes are written
+ *   kv_buf         bf16 [num_slots, 576], 16-byte aligned, written at the
+ *                  draft tokens' slots
+ *   kv_indices     int32 [total_kv], kv_indptr int32 [B+1]: written
+ *   mask           uint8 [total_mask] (needed with parents), mask_indptr
+ *                  int32 [B+1] (written if not NULL; needed with parents)
+ *
+ * All pointers are device memory owned by the caller.  Host-detectable errors
+ * (NULL where required, sizes out of range, misalignment) return TV_ERR_*
+ * before anything is enqueued.  Device contents that break the preconditions
+ * (decreasing indptrs, lengths above the bounds, slots outside the pool,
+ * parents out of order, totals above the capacities) give undefined contents
+ * but no store outside the buffers: every store is bounded by the capacities
+ * above, a draft row whose slot is outside the pool is not written, and a
+ * parent out of order ends that row's ancestor walk.  Draft tokens sharing a
+ * slot race.
+ */
+tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
+                          const int32_t* out_cache_loc, const int32_t* prefix_indices,
+                          const int32_t* prefix_indptr, const int32_t* qo_indptr,
+                          const int32_t* parents, void* kv_buf, int32_t* kv_indices,
+                          int32_t* kv_indptr, uint8_t* mask, int32_t* mask_indptr,
+                          void* stream);
+
 /* Static description of a status code. */
 const char* tv_status_str(tv_status s);
 

@@ -197,3 +197,43 @@ def test_problem_struct_layout_matches_header():
     assert tv.Problem.num_splits.offset == 48 and tv.Problem.out_dtype.offset == 52
     assert tv.Problem.flags.offset == 56 and tv.Problem.reserved.offset == 60
     assert ctypes.sizeof(tv.Plan) == 24
+
+
+def aprob(**kw):
+    base = dict(batch=1, max_q_len=9, max_kv_len=30, total_q=9, num_slots=4096, total_prefix=21,
+                total_kv=30, total_mask=270, flags=0)
+    base.update(kw)
+    return tv.make_append_problem(**base)
+
+
+def test_append_problem_layout():
+    assert ctypes.sizeof(tv.AppendProblem) == 56
+    assert tv.AppendProblem.total_q.offset == 16 and tv.AppendProblem.total_mask.offset == 48
+
+
+def test_append_draft_argument_errors_before_any_launch():
+    fake = 1 << 20  # aligned non-null stand-in; never dereferenced on these paths
+    args = [fake] * 11  # draft_kv .. mask_indptr
+    # sizes
+    for kw, code in [(dict(batch=-1), 2), (dict(total_kv=2 ** 31), 2), (dict(max_q_len=40), 2),
+                     (dict(max_kv_len=1 << 30, max_q_len=9), 2), (dict(flags=1), 4),
+                     (dict(flags=8), 4)]:
+        assert tv.append_draft_status(aprob(**kw), *args) == code, kw
+    # nothing to do: no launch, no pointer needed
+    assert tv.append_draft_status(aprob(batch=0), *([0] * 11)) == 0
+    # required pointers: prefix_indptr, qo_indptr, kv_indptr, out_cache_loc, ...
+    for i in (1, 3, 4, 8, 9):
+        a = list(args)
+        a[i] = 0
+        assert tv.append_draft_status(aprob(), *a) == 1, i
+    # parents without a mask; draft rows without a pool
+    a = list(args)
+    a[9] = 0
+    assert tv.append_draft_status(aprob(), *a) == 1
+    a = list(args)
+    a[6] = 0
+    assert tv.append_draft_status(aprob(), *a) == 1
+    # misaligned rows
+    a = list(args)
+    a[0] = fake + 8
+    assert tv.append_draft_status(aprob(), *a) == 2

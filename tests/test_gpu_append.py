@@ -1,0 +1,150 @@
+"""The marshaling step on the GPU (tv_append_draft through the C ABI) against
+its oracle (oracle/marshal.py): key lists, indptrs, mask bytes and pool rows
+must match bit for bit; the verify call on what the step built must then match
+the attention oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.marshal as M
+import tv_workload as W
+from gpu_util import compare, run
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU present", allow_module_level=True)
+
+import tree_verify_mla_paged_amd as tv  # noqa: E402  (fails loudly if the library is missing)
+
+SENT_I32 = -7
+SENT_U8 = 0xEE
+
+
+def dev(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if a.size == 0:
+        a = np.zeros(1, dtype=dtype)
+    return torch.from_numpy(a.view(np.int16) if dtype == np.uint16 else a).to("cuda")
+
+
+def gpu_append(w, prefix_visible=False, with_rows=True, with_parents=True, kv_cap=None,
+               mask_cap=None, guard=64, parents=None):
+    """Runs tv_append_draft on the pieces of workload w; returns host arrays
+    (pool, kv_indices incl. guard, kv_indptr, mask incl. guard, mask_indptr)."""
+    x = W.marshal_inputs(w)
+    if parents is not None:
+        x["parents"] = parents
+    B = w.batch
+    need_kv = int(w.kv_lens.sum())
+    n, L = w.q_lens, w.kv_lens
+    need_mask = int((n * (n if prefix_visible else L)).sum())
+    kv_cap = need_kv if kv_cap is None else kv_cap
+    mask_cap = need_mask if mask_cap is None else mask_cap
+    pool = dev(x["kv_buf"], np.uint16)
+    t = dict(draft_kv=dev(x["draft_kv"], np.uint16), out_cache_loc=dev(x["out_cache_loc"], np.int32),
+             prefix_indices=dev(x["prefix_indices"], np.int32),
+             prefix_indptr=dev(x["prefix_indptr"], np.int32), qo_indptr=dev(x["qo_indptr"], np.int32),
+             parents=dev(x["parents"], np.int32))
+    kv_indices = torch.full((kv_cap + guard,), SENT_I32, dtype=torch.int32, device="cuda")
+    kv_indptr = torch.full((B + 1,), SENT_I32, dtype=torch.int32, device="cuda")
+    mask = torch.full((mask_cap + guard,), SENT_U8, dtype=torch.uint8, device="cuda")
+    mask_indptr = torch.full((B + 1,), SENT_I32, dtype=torch.int32, device="cuda")
+    p = tv.make_append_problem(B, w.max_q_len, w.max_kv_len, w.total_q, w.num_slots,
+                               int(x["prefix_indices"].size), kv_cap, mask_cap,
+                               tv.FLAG_PREFIX_VISIBLE if prefix_visible else 0)
+    tv.append_draft(p, t["draft_kv"] if with_rows else None, t["out_cache_loc"],
+                    t["prefix_indices"], t["prefix_indptr"], t["qo_indptr"],
+                    t["parents"] if with_parents else None, pool, kv_indices, kv_indptr,
+                    mask, mask_indptr)
+    torch.cuda.synchronize()
+    return (x, pool.cpu().numpy().view(np.uint16), kv_indices.cpu().numpy(),
+            kv_indptr.cpu().numpy(), mask.cpu().numpy(), mask_indptr.cpu().numpy())
+
+
+def expected(x, prefix_visible=False):
+    return M.append_draft(x["kv_buf"], x["draft_kv"], x["out_cache_loc"], x["prefix_indices"],
+                          x["prefix_indptr"], x["qo_indptr"], x["parents"],
+                          prefix_visible=prefix_visible)
+
+
+WORKLOADS = {
+    "C1": lambda: W.config(1),
+    "C2": lambda: W.config(2),
+    "batch-with-empty": lambda: W.small(501, [300, 7, 0, 95, 0], [3, 2, 0, 6, 1], 2),
+    "chain": lambda: W.chain(502, [1000, 3], 40, 1),
+    "C3": lambda: W.config(3),
+    "C5": lambda: W.config(5),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("prefix_visible", [False, True])
+def test_append_matches_oracle(name, prefix_visible):
+    print("append %s prefix_visible=%s" % (name, prefix_visible), flush=True)
+    w = WORKLOADS[name]()
+    x, pool, ki, kp, m, mp = gpu_append(w, prefix_visible=prefix_visible)
+    ekv, eki, ekp, em, emp = expected(x, prefix_visible)
+    nk, nm = eki.size, em.size
+    assert np.array_equal(kp, ekp)
+    assert np.array_equal(ki[:nk], eki) and np.all(ki[nk:] == SENT_I32)
+    assert np.array_equal(mp, emp)
+    assert np.array_equal(m[:nm], em) and np.all(m[nm:] == SENT_U8)
+    assert np.array_equal(pool, ekv)
+    # and the generator's own layout
+    assert np.array_equal(ki[:nk], w.kv_indices)
+    assert np.array_equal(pool, w.kv)
+
+
+@pytest.mark.parametrize("prefix_visible", [False, True])
+def test_verify_on_what_append_built(prefix_visible):
+    """The pages' parity failure was in this step; the whole chain must match."""
+    print("append + verify prefix_visible=%s" % prefix_visible, flush=True)
+    w = W.config(2)
+    x, pool, ki, kp, m, mp = gpu_append(w, prefix_visible=prefix_visible, guard=0)
+    import dataclasses
+    built = dataclasses.replace(w, kv=pool, kv_indices=ki, kv_indptr=kp, mask=m, mask_indptr=mp,
+                                prefix_visible=prefix_visible)
+    o, l = run(built, out_f32=True)
+    ro, rl = oracle.run(w)
+    compare(o, l, ro, rl, bf16_out=False, label="append+verify")
+
+
+def test_append_stores_stay_within_capacities():
+    """Capacities below what the indptrs need: the stores stop at them."""
+    print("append with short capacities", flush=True)
+    w = W.config(2)
+    need_kv = int(w.kv_lens.sum())
+    need_mask = int(w.mask.size)
+    x, pool, ki, kp, m, mp = gpu_append(w, kv_cap=need_kv - 5, mask_cap=need_mask - 7, guard=64)
+    ekv, eki, ekp, em, emp = expected(x)
+    assert np.array_equal(ki[:need_kv - 5], eki[:need_kv - 5]) and np.all(ki[need_kv - 5:] == SENT_I32)
+    assert np.array_equal(m[:need_mask - 7], em[:need_mask - 7]) and np.all(m[need_mask - 7:] == SENT_U8)
+    assert np.array_equal(kp, ekp) and np.array_equal(mp, emp)
+
+
+def test_append_without_rows_or_mask():
+    """draft_kv NULL leaves the pool alone; parents NULL writes no mask byte
+    (mask_indptr is still the running sum of the blocks)."""
+    print("append without rows or parents", flush=True)
+    w = W.config(2)
+    x, pool, ki, kp, m, mp = gpu_append(w, with_rows=False, with_parents=False)
+    ekv, eki, ekp, em, emp = expected(x)
+    assert np.array_equal(pool, x["kv_buf"])
+    assert np.array_equal(ki[:eki.size], eki) and np.array_equal(kp, ekp)
+    assert np.all(m == SENT_U8) and np.array_equal(mp, emp)
+
+
+def test_append_parent_out_of_order_ends_the_walk():
+    """A parent link that does not point to an earlier draft ends that row's
+    ancestor walk as a root would: the row sees its path up to the bad link."""
+    print("append with a parent out of order", flush=True)
+    w = W.chain(503, [10], 6, 1)
+    parents = np.array([-1, 0, 1, 3, 3, 4], dtype=np.int32)  # draft 3 names itself
+    x, pool, ki, kp, m, mp = gpu_append(w, parents=parents, guard=0)
+    rows = m.reshape(6, 16)
+    assert np.all(rows[:, :10] == 1)
+    expect = np.array([[1, 0, 0, 0, 0, 0], [1, 1, 0, 0, 0, 0], [1, 1, 1, 0, 0, 0],
+                       [0, 0, 0, 1, 0, 0], [0, 0, 0, 1, 1, 0], [0, 0, 0, 1, 1, 1]], np.uint8)
+    assert np.array_equal(rows[:, 10:], expect)

@@ -494,3 +494,64 @@ def test_prefix_visible_form_needs_a_visible_prefix():
     w.mask[0] = 0
     with pytest.raises(ValueError):
         W.prefix_visible_form(w)
+
+
+# ------------------------------------------------ the marshaling step
+
+import oracle.marshal as M  # noqa: E402
+
+
+def marshal(w, prefix_visible=False, parents=True):
+    x = W.marshal_inputs(w)
+    return M.append_draft(x["kv_buf"], x["draft_kv"], x["out_cache_loc"], x["prefix_indices"],
+                          x["prefix_indptr"], x["qo_indptr"],
+                          x["parents"] if parents else None, prefix_visible=prefix_visible)
+
+
+@pytest.mark.parametrize("make", [lambda: W.config(1), lambda: W.config(2),
+                                  lambda: W.small(41, [300, 7, 0, 95], [3, 2, 0, 6], 2),
+                                  lambda: W.chain(42, [5, 0], 4, 1)])
+def test_marshal_rebuilds_the_generated_inputs(make):
+    """The generator lays out keys and masks by its own route (per-request tree
+    masks from ancestor lists); the step's definition must rebuild them exactly
+    from the pieces, and put the draft rows back into the pool."""
+    w = make()
+    kv, ki, kp, m, mp = marshal(w)
+    assert np.array_equal(ki, w.kv_indices) and np.array_equal(kp, w.kv_indptr)
+    assert np.array_equal(m, w.mask) and np.array_equal(mp, w.mask_indptr)
+    assert np.array_equal(kv.view(np.uint16), w.kv.view(np.uint16))
+    kv, ki, kp, m, mp = marshal(w, prefix_visible=True)
+    pv = W.prefix_visible_form(w)
+    assert np.array_equal(m, pv.mask) and np.array_equal(mp, pv.mask_indptr)
+    _, _, _, m, mp = marshal(w, parents=False)
+    assert m is None and mp is None
+
+
+def test_marshal_live_shape():
+    """The pages' live call: 9 drafts after a 21-token prefix give a 270-byte
+    mask at row stride 30 and 30 keys, the draft slots last."""
+    live = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "live_shapes.json")))
+    w = W.config(1)
+    x = W.marshal_inputs(w)
+    kv, ki, kp, m, mp = marshal(w)
+    n, P = live["n_draft"], live["prefix_len"]
+    assert m.size == live["mask"][0] == n * (P + n)
+    assert int(kp[-1]) == P + n and np.array_equal(ki[P:], x["out_cache_loc"])
+
+
+def test_marshal_mask_closed_forms():
+    """Row i of the full form has P + depth(i) ones; a chain gives a lower
+    triangle over the draft keys, a star (every node a child of node 0) the
+    diagonal plus column 0."""
+    P, n = 5, 6
+    star = np.eye(n, dtype=np.uint8)
+    star[:, 0] = 1
+    for parents, block in [(np.arange(-1, n - 1), np.tril(np.ones((n, n), np.uint8))),
+                           (np.array([-1] + [0] * (n - 1)), star)]:
+        w = W.build(43, [P], [parents], 1, 64)
+        kv, ki, kp, m, mp = marshal(w)
+        rows = m.reshape(n, P + n)
+        assert np.all(rows[:, :P] == 1)
+        depth = [len(W.ancestors_and_self(parents, i)) for i in range(n)]
+        assert list(rows.sum(axis=1)) == [P + d for d in depth]
+        assert np.array_equal(rows[:, P:], block)

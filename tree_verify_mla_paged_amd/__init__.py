@@ -24,7 +24,7 @@ STATUS = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_WORKSPACE"
           4: "TV_ERR_UNSUPPORTED", 5: "TV_ERR_INPUT", 6: "TV_ERR_LAUNCH", 7: "TV_ERR_HIP"}
 
 EXPORTS = ("tv_get_plan", "tv_workspace_bytes", "tv_verify_attn", "tv_verify_attn_timed",
-           "tv_check_inputs",
+           "tv_check_inputs", "tv_append_draft",
            "tv_status_str")
 
 
@@ -35,6 +35,14 @@ class Problem(ctypes.Structure):
                 ("total_kv", ctypes.c_int64), ("total_mask", ctypes.c_int64),
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class AppendProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("num_slots", ctypes.c_int64),
+                ("total_prefix", ctypes.c_int64), ("total_kv", ctypes.c_int64),
+                ("total_mask", ctypes.c_int64)]
 
 
 class Plan(ctypes.Structure):
@@ -74,6 +82,8 @@ _lib.tv_verify_attn_timed.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, cty
 _lib.tv_verify_attn_timed.restype = ctypes.c_int
 _lib.tv_check_inputs.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_int32)]
 _lib.tv_check_inputs.restype = ctypes.c_int
+_lib.tv_append_draft.argtypes = [ctypes.POINTER(AppendProblem)] + [_vp] * 12
+_lib.tv_append_draft.restype = ctypes.c_int
 _lib.tv_status_str.argtypes = [ctypes.c_int]
 _lib.tv_status_str.restype = ctypes.c_char_p
 
@@ -167,3 +177,35 @@ def check_inputs(problem: Problem, kv_indices, kv_indptr, qo_indptr, mask_indptr
                               _ptr(qo_indptr), _ptr(mask_indptr), _stream(stream),
                               ctypes.byref(bad))
     return int(rc), int(bad.value)
+
+
+def make_append_problem(batch: int, max_q_len: int, max_kv_len: int, total_q: int,
+                        num_slots: int, total_prefix: int, total_kv: int, total_mask: int,
+                        flags: int = 0) -> AppendProblem:
+    return AppendProblem(batch, max_q_len, max_kv_len, flags, total_q, num_slots, total_prefix,
+                         total_kv, total_mask)
+
+
+def append_draft_status(problem: AppendProblem, draft_kv, out_cache_loc, prefix_indices,
+                        prefix_indptr, qo_indptr, parents, kv_buf, kv_indices, kv_indptr, mask,
+                        mask_indptr, stream=None) -> int:
+    """tv_append_draft, returning the raw status code."""
+    return int(_lib.tv_append_draft(ctypes.byref(problem), _ptr(draft_kv), _ptr(out_cache_loc),
+                                    _ptr(prefix_indices), _ptr(prefix_indptr), _ptr(qo_indptr),
+                                    _ptr(parents), _ptr(kv_buf), _ptr(kv_indices),
+                                    _ptr(kv_indptr), _ptr(mask), _ptr(mask_indptr),
+                                    _stream(stream) if stream is not None else 0))
+
+
+def append_draft(problem: AppendProblem, draft_kv, out_cache_loc, prefix_indices, prefix_indptr,
+                 qo_indptr, parents, kv_buf, kv_indices, kv_indptr, mask, mask_indptr,
+                 stream=None):
+    """Enqueue tv_append_draft on `stream` (default: torch's current stream):
+    draft rows into the pool, kv_indices / kv_indptr, and (with parents) the
+    tree mask and mask_indptr."""
+    rc = _lib.tv_append_draft(ctypes.byref(problem), _ptr(draft_kv), _ptr(out_cache_loc),
+                              _ptr(prefix_indices), _ptr(prefix_indptr), _ptr(qo_indptr),
+                              _ptr(parents), _ptr(kv_buf), _ptr(kv_indices), _ptr(kv_indptr),
+                              _ptr(mask), _ptr(mask_indptr), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tv_append_draft")

@@ -27,6 +27,9 @@ static_assert(sizeof(tv_problem) == 64 && offsetof(tv_problem, total_q) == 8 &&
               "tv_problem layout is part of the ABI");
 static_assert(sizeof(tv_plan) == 24 && offsetof(tv_plan, workspace_bytes) == 16,
               "tv_plan layout is part of the ABI");
+static_assert(sizeof(tv_append_problem) == 56 && offsetof(tv_append_problem, total_q) == 16 &&
+                  offsetof(tv_append_problem, total_mask) == 48,
+              "tv_append_problem layout is part of the ABI");
 
 namespace {
 
@@ -338,6 +341,65 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
       }
     }
   }
+  return TV_OK;
+}
+
+tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
+                          const int32_t* out_cache_loc, const int32_t* prefix_indices,
+                          const int32_t* prefix_indptr, const int32_t* qo_indptr,
+                          const int32_t* parents, void* kv_buf, int32_t* kv_indices,
+                          int32_t* kv_indptr, uint8_t* mask, int32_t* mask_indptr,
+                          void* stream) {
+  if (!p) return TV_ERR_NULL;
+  if (p->batch < 0 || p->max_q_len < 0 || p->max_kv_len < 0 || p->total_q < 0 ||
+      p->num_slots < 0 || p->total_prefix < 0 || p->total_kv < 0 || p->total_mask < 0)
+    return TV_ERR_SHAPE;
+  if ((p->flags & ~TV_FLAG_PREFIX_VISIBLE) != 0) return TV_ERR_UNSUPPORTED;
+  if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->total_prefix > kMaxInt32 ||
+      p->total_q > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL || p->max_q_len > p->max_kv_len ||
+      p->max_kv_len >= (1 << 30) || p->batch >= (1 << 16))
+    return TV_ERR_SHAPE;
+  if (p->batch == 0) return TV_OK;
+  if (!prefix_indptr || !qo_indptr || !kv_indptr) return TV_ERR_NULL;
+  if (p->total_q > 0 && !out_cache_loc) return TV_ERR_NULL;
+  if (p->total_prefix > 0 && !prefix_indices) return TV_ERR_NULL;
+  if (p->total_kv > 0 && !kv_indices) return TV_ERR_NULL;
+  if (draft_kv && !kv_buf) return TV_ERR_NULL;
+  if (parents && (!mask || !mask_indptr)) return TV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(draft_kv) & 15) || (reinterpret_cast<uintptr_t>(kv_buf) & 15))
+    return TV_ERR_SHAPE;
+  const bool pv = (p->flags & TV_FLAG_PREFIX_VISIBLE) != 0;
+  tv::AppendParams ap;
+  ap.draft_kv = static_cast<const uint16_t*>(draft_kv);
+  ap.out_cache_loc = out_cache_loc;
+  ap.prefix_indices = prefix_indices;
+  ap.prefix_indptr = prefix_indptr;
+  ap.qo_indptr = qo_indptr;
+  ap.parents = parents;
+  ap.kv_buf = static_cast<uint16_t*>(kv_buf);
+  ap.kv_indices = kv_indices;
+  ap.kv_indptr = kv_indptr;
+  ap.mask = mask;
+  ap.mask_indptr = mask_indptr;
+  ap.total_q = p->total_q;
+  ap.num_slots = p->num_slots;
+  ap.total_prefix = p->total_prefix;
+  ap.total_kv = p->total_kv;
+  ap.total_mask = p->total_mask;
+  ap.batch = p->batch;
+  ap.max_q_len = p->max_q_len;
+  ap.max_kv_len = p->max_kv_len;
+  ap.prefix_visible = pv ? 1 : 0;
+  // fill-kernel workgroup ranges: draft rows (72 16-byte pieces each),
+  // kv_indices (256 keys each), mask rows (256 bytes each)
+  ap.rows_x = draft_kv ? (int32_t)ceil_div((int64_t)p->max_q_len * (TV_QK_DIM * 2 / 16), 256) : 0;
+  ap.idx_x = (int32_t)ceil_div(p->max_kv_len, 256);
+  ap.mask_chunks = (int32_t)std::max<int64_t>(1, ceil_div(pv ? p->max_q_len : p->max_kv_len, 256));
+  const int64_t grid = (int64_t)ap.rows_x + ap.idx_x +
+                       (parents ? (int64_t)p->max_q_len * ap.mask_chunks : 0);
+  if (grid > kMaxInt32) return TV_ERR_SHAPE;
+  if (tv::launch_append(ap, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TV_ERR_LAUNCH;
   return TV_OK;
 }
 

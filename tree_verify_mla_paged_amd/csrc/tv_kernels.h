@@ -96,6 +96,26 @@ struct MergeParams {
   int32_t max_splits;
 };
 
+// The marshaling step (tv_append_draft): see tv_append.hip.
+struct AppendParams {
+  const uint16_t* draft_kv;       // bf16 [total_q, 576] or null (no pool write)
+  const int32_t* out_cache_loc;   // [total_q] pool slot of each draft token
+  const int32_t* prefix_indices;  // [total_prefix]
+  const int32_t* prefix_indptr;   // [batch + 1]
+  const int32_t* qo_indptr;       // [batch + 1]
+  const int32_t* parents;         // [total_q] request-local parent, -1 root; null: no mask
+  uint16_t* kv_buf;               // bf16 [num_slots, 576]
+  int32_t* kv_indices;            // [total_kv]
+  int32_t* kv_indptr;             // [batch + 1]
+  uint8_t* mask;                  // [total_mask]
+  int32_t* mask_indptr;           // [batch + 1]
+  int64_t total_q, num_slots, total_prefix, total_kv, total_mask;
+  int32_t batch, max_q_len, max_kv_len;
+  int32_t prefix_visible;         // mask in the n x n form
+  int32_t rows_x, idx_x, mask_chunks;  // fill-kernel workgroup ranges (see tv_append.hip)
+};
+
+hipError_t launch_append(const AppendParams& p, int grid_x, hipStream_t st);
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st);
 // ev0 / ev1 (may be null): stamped with the split kernel's own start and end.
 hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent_t ev0,

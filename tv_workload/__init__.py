@@ -344,3 +344,31 @@ def extra(key: str, poison: bool = True) -> Workload:
     if key == "K":
         return chain(302, [32768], 16, 16, pool=200000, poison=poison, name="K")
     raise ValueError("unknown workload %r" % key)
+
+
+def marshal_inputs(w: Workload) -> dict:
+    """A generated workload taken apart into the inputs of the marshaling step
+    (draft rows into the pool, key lists, tree mask): the pool without the draft
+    rows (bf16 NaN there), the draft rows, their slots, the prefix slot lists,
+    the prefix indptr, qo_indptr and the parents.  The workload's own kv_indices,
+    indptrs and mask are what the step must rebuild from them."""
+    B = w.batch
+    qo = w.qo_indptr.astype(np.int64)
+    kvp = w.kv_indptr.astype(np.int64)
+    n = np.diff(qo)
+    P = np.diff(kvp) - n
+    prefix_indptr = np.zeros(B + 1, dtype=np.int64)
+    prefix_indptr[1:] = np.cumsum(P)
+    prefix = [w.kv_indices[kvp[b]:kvp[b] + P[b]] for b in range(B)]
+    draft = [w.kv_indices[kvp[b] + P[b]:kvp[b + 1]] for b in range(B)]
+    prefix_indices = np.concatenate(prefix) if B else np.zeros(0, np.int32)
+    out_cache_loc = np.concatenate(draft) if B else np.zeros(0, np.int32)
+    draft_kv = w.kv[out_cache_loc].copy()
+    pool = w.kv.copy()
+    pool[out_cache_loc] = BF16_NAN
+    parents = np.concatenate([np.asarray(p, dtype=np.int32) for p in w.parents]) if B else \
+        np.zeros(0, np.int32)
+    return dict(kv_buf=pool, draft_kv=draft_kv, out_cache_loc=out_cache_loc.astype(np.int32),
+                prefix_indices=prefix_indices.astype(np.int32),
+                prefix_indptr=prefix_indptr.astype(np.int32), qo_indptr=w.qo_indptr.copy(),
+                parents=parents)
