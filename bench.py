@@ -213,6 +213,51 @@ def write_traffic(args):
     print(json.dumps(d["workloads"][key], indent=1))
 
 
+def append_times(w, steps, prefix_visible):
+    """tv_append_draft (draft rows into the pool, key lists, indptrs, tree mask)
+    on the workload's pieces, timed back to back; algorithmic bytes: the draft
+    rows read and written, the slot lists read, kv_indices and the mask
+    written, the parents read."""
+    import torch
+    import tree_verify_mla_paged_amd as tv
+    x = W.marshal_inputs(w)
+
+    def dev(a, dt):
+        a = np.ascontiguousarray(a, dtype=dt)
+        a = a if a.size else np.zeros(1, dt)
+        return torch.from_numpy(a.view(np.int16) if dt == np.uint16 else a).to("cuda")
+
+    t = {k: dev(x[k], np.uint16 if k in ("kv_buf", "draft_kv") else np.int32)
+         for k in ("kv_buf", "draft_kv", "out_cache_loc", "prefix_indices", "prefix_indptr",
+                   "qo_indptr", "parents")}
+    n, L = w.q_lens, w.kv_lens
+    nmask = int((n * (n if prefix_visible else L)).sum())
+    ki = torch.empty(int(L.sum()) + 1, dtype=torch.int32, device="cuda")
+    kp = torch.empty(w.batch + 1, dtype=torch.int32, device="cuda")
+    m = torch.empty(nmask + 1, dtype=torch.uint8, device="cuda")
+    mp = torch.empty(w.batch + 1, dtype=torch.int32, device="cuda")
+    p = tv.make_append_problem(w.batch, w.max_q_len, w.max_kv_len, w.total_q, w.num_slots,
+                               int(x["prefix_indices"].size), int(L.sum()), nmask,
+                               tv.FLAG_PREFIX_VISIBLE if prefix_visible else 0)
+
+    def call():
+        tv.append_draft(p, t["draft_kv"], t["out_cache_loc"], t["prefix_indices"],
+                        t["prefix_indptr"], t["qo_indptr"], t["parents"], t["kv_buf"], ki, kp,
+                        m, mp)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    N = int(w.total_q)
+    nbytes = 2 * N * 1152 + N * 4 + int((L - n).sum()) * 4 + int(L.sum()) * 4 + nmask + N * 4
+    return {"us_per_call": us, "bytes": nbytes, "GB/s": nbytes / us / 1e3,
+            "mask_form": "prefix-visible" if prefix_visible else "full"}
+
+
 SCRUB_BYTES = 1 << 30  # larger than the 256 MB MALL plus every XCD's L2
 
 
@@ -296,6 +341,8 @@ def main():
     ap.add_argument("--config", default="3",
                     help="1-5 (benchmark configurations), S1-S3 (long-prefix sweep), "
                          "D (plain decode) or K (chain verify)")
+    ap.add_argument("--append", action="store_true",
+                    help="also time tv_append_draft (the marshaling step) on the same workload")
     ap.add_argument("--prefix-visible", action="store_true",
                     help="pass the mask in the prefix-visible form (draft keys only)")
     ap.add_argument("--splits", type=int, default=0,
@@ -402,6 +449,7 @@ def main():
     graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
 
     cold = cold_cache_times(call, stream, args.cold_calls) if args.cold_calls > 0 else None
+    append = append_times(w, args.steps, args.prefix_visible) if args.append else None
 
     kv_bytes, total_bytes, flops = algorithmic(w)
     us_per_call = ms_per_step * 1e3
@@ -433,6 +481,7 @@ def main():
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "graph_us_per_call": graph_us,
         "cold_cache": cold,
+        "append_draft": append,
         "floor_fraction": max(t_hbm, t_mfma) / (ms_per_step * 1e-3),
         "config": {"workload": desc, "requests": w.batch, "n_draft": int(w.max_q_len),
                    "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,

@@ -240,7 +240,7 @@ typedef struct tv_append_problem {
  *   kv_buf         bf16 [num_slots, 576], 16-byte aligned, written at the
  *                  draft tokens' slots
  *   kv_indices     int32 [total_kv], kv_indptr int32 [B+1]: written
- *   mask           uint8 [total_mask] (needed with parents), mask_indptr
+ *   mask           uint8 [total_mask], 16-byte aligned (needed with parents), mask_indptr
  *                  int32 [B+1] (written if not NULL; needed with parents)
  *
  * All pointers are device memory owned by the caller.  Host-detectable errors

@@ -366,7 +366,8 @@ tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
   if (p->total_kv > 0 && !kv_indices) return TV_ERR_NULL;
   if (draft_kv && !kv_buf) return TV_ERR_NULL;
   if (parents && (!mask || !mask_indptr)) return TV_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(draft_kv) & 15) || (reinterpret_cast<uintptr_t>(kv_buf) & 15))
+  if ((reinterpret_cast<uintptr_t>(draft_kv) & 15) || (reinterpret_cast<uintptr_t>(kv_buf) & 15) ||
+      (reinterpret_cast<uintptr_t>(mask) & 15))
     return TV_ERR_SHAPE;
   const bool pv = (p->flags & TV_FLAG_PREFIX_VISIBLE) != 0;
   tv::AppendParams ap;
@@ -394,9 +395,13 @@ tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
   // kv_indices (256 keys each), mask rows (256 bytes each)
   ap.rows_x = draft_kv ? (int32_t)ceil_div((int64_t)p->max_q_len * (TV_QK_DIM * 2 / 16), 256) : 0;
   ap.idx_x = (int32_t)ceil_div(p->max_kv_len, 256);
-  ap.mask_chunks = (int32_t)std::max<int64_t>(1, ceil_div(pv ? p->max_q_len : p->max_kv_len, 256));
-  const int64_t grid = (int64_t)ap.rows_x + ap.idx_x +
-                       (parents ? (int64_t)p->max_q_len * ap.mask_chunks : 0);
+  // 16 mask bytes per thread over the largest block, plus a word for its
+  // unaligned start
+  const int64_t block_words =
+      ceil_div((int64_t)p->max_q_len * (pv ? p->max_q_len : p->max_kv_len), 16) + 1;
+  if (block_words > kMaxInt32) return TV_ERR_SHAPE;
+  ap.mask_x = (int32_t)ceil_div(block_words, 256);
+  const int64_t grid = (int64_t)ap.rows_x + ap.idx_x + (parents ? ap.mask_x : 0);
   if (grid > kMaxInt32) return TV_ERR_SHAPE;
   if (tv::launch_append(ap, (int)grid, static_cast<hipStream_t>(stream)) != hipSuccess)
     return TV_ERR_LAUNCH;

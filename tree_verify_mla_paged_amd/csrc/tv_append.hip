@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256) void tv_append_scan_kernel(AppendParams p) {
 //                          (3.5 rows per workgroup pass), draft t to pool row
 //                          out_cache_loc[t];
 //   [rows_x, rows_x+idx_x) kv_indices of request b, 256 keys per workgroup;
-//   [rows_x+idx_x, ...)    the mask block of request b, 256 bytes of one draft
-//                          row per workgroup: prefix keys 1, draft key k of row
-//                          i 1 iff k is i or one of its ancestors.
+//   [rows_x+idx_x, ...)    the mask block of request b, 16 bytes per thread:
+//                          prefix keys 1, draft key k of row i 1 iff k is i or
+//                          one of its ancestors.
 __global__ __launch_bounds__(256) void tv_append_fill_kernel(AppendParams p) {
   const int b = blockIdx.y;
   const int t = threadIdx.x;
@@ -114,35 +114,59 @@ __global__ __launch_bounds__(256) void tv_append_fill_kernel(AppendParams p) {
   }
   x -= p.idx_x;
   if (!p.parents || !p.mask || !p.mask_indptr) return;
-  // one draft row per workgroup-row of chunks: x = i * mask_chunks + chunk
-  const int i = x / p.mask_chunks;
-  const int chunk = x - i * p.mask_chunks;
-  if (i >= n) return;
+  // the request's mask block as 16-byte words (offsets from the 16-byte
+  // aligned mask base); a word wholly inside the block and the capacity is one
+  // 16-byte store, a word the block shares with a neighbour is stored bytewise
   const int stride = p.prefix_visible ? n : P + n;
   const int skip = p.prefix_visible ? 0 : P;  // columns before the draft keys
-  const int64_t row0 = (int64_t)p.mask_indptr[b] + (int64_t)i * stride;
-  for (int j = chunk * 256 + t; j < stride; j += p.mask_chunks * 256) {
-    const int64_t dst = row0 + j;
-    if (dst < 0 || dst >= p.total_mask) continue;
-    uint8_t vis = 1;
-    if (j >= skip) {
-      // draft key k: walk up from row i; parents precede children, so the
-      // walk descends and ends within i + 1 steps (a parent that breaks the
-      // order ends it, as a root would)
-      const int k = j - skip;
-      int a = i;
-      for (int step = 0; step <= i && a > k; ++step) {
-        const int64_t tok = (int64_t)q0 + a;
-        const int pa = (tok >= 0 && tok < p.total_q) ? p.parents[tok] : -1;
-        if (pa < -1 || pa >= a) {
-          a = -1;
-          break;
+  const int64_t blk0 = p.mask_indptr[b];
+  const int64_t lim = min(blk0 + (int64_t)n * stride, p.total_mask);
+  if (blk0 < 0 || lim <= blk0 || stride <= 0) return;
+  const int64_t w0 = blk0 >> 4;
+  const int64_t nw = ((lim + 15) >> 4) - w0;
+  for (int64_t wi = (int64_t)x * 256 + t; wi < nw; wi += (int64_t)p.mask_x * 256) {
+    const int64_t a0 = (w0 + wi) << 4;
+    // row and column of the word's first byte inside the block
+    const int64_t off0 = max(a0, blk0) - blk0;
+    int i = (int)(off0 / stride);
+    int j = (int)(off0 - (int64_t)i * stride);
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t a = a0 + e;
+      if (a < blk0 || a >= lim) continue;
+      uint32_t vis = 1;
+      if (j >= skip) {
+        // draft key k: walk up from row i; parents precede children, so the
+        // walk descends and ends within i + 1 steps (a parent that breaks the
+        // order ends it, as a root would)
+        const int k = j - skip;
+        int anc = i;
+        for (int step = 0; step <= i && anc > k; ++step) {
+          const int64_t tok = (int64_t)q0 + anc;
+          const int pa = (tok >= 0 && tok < p.total_q) ? p.parents[tok] : -1;
+          if (pa < -1 || pa >= anc) {
+            anc = -1;
+            break;
+          }
+          anc = pa;
         }
-        a = pa;
+        vis = anc == k ? 1u : 0u;
       }
-      vis = a == k ? 1 : 0;
+      word[e >> 2] |= vis << (8 * (e & 3));
+      if (++j == stride) {
+        j = 0;
+        ++i;
+      }
     }
-    p.mask[dst] = vis;
+    if (a0 >= blk0 && a0 + 16 <= lim) {
+      reinterpret_cast<uint4*>(p.mask)[w0 + wi] = make_uint4(word[0], word[1], word[2], word[3]);
+    } else {
+      for (int e = 0; e < 16; ++e) {
+        const int64_t a = a0 + e;
+        if (a >= blk0 && a < lim) p.mask[a] = (uint8_t)(word[e >> 2] >> (8 * (e & 3)));
+      }
+    }
   }
 }
 

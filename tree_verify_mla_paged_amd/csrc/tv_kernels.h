@@ -112,7 +112,7 @@ struct AppendParams {
   int64_t total_q, num_slots, total_prefix, total_kv, total_mask;
   int32_t batch, max_q_len, max_kv_len;
   int32_t prefix_visible;         // mask in the n x n form
-  int32_t rows_x, idx_x, mask_chunks;  // fill-kernel workgroup ranges (see tv_append.hip)
+  int32_t rows_x, idx_x, mask_x;  // fill-kernel workgroup ranges (see tv_append.hip)
 };
 
 hipError_t launch_append(const AppendParams& p, int grid_x, hipStream_t st);
