@@ -148,3 +148,69 @@ def test_append_parent_out_of_order_ends_the_walk():
     expect = np.array([[1, 0, 0, 0, 0, 0], [1, 1, 0, 0, 0, 0], [1, 1, 1, 0, 0, 0],
                        [0, 0, 0, 1, 0, 0], [0, 0, 0, 1, 1, 0], [0, 0, 0, 1, 1, 1]], np.uint8)
     assert np.array_equal(rows[:, 10:], expect)
+
+
+def test_append_and_verify_captured_in_one_graph():
+    """Both entry points only enqueue kernels: the marshaling step and the
+    verify call captured together in one HIP graph replay to the eager result,
+    with eager work between replays, and follow new draft rows."""
+    from gpu_util import GpuCall
+    print("append + verify in one graph", flush=True)
+    w = W.config(2)
+    x = W.marshal_inputs(w)
+    B = w.batch
+    pieces = dict(draft_kv=dev(x["draft_kv"], np.uint16), out_cache_loc=dev(x["out_cache_loc"], np.int32),
+                  prefix_indices=dev(x["prefix_indices"], np.int32),
+                  prefix_indptr=dev(x["prefix_indptr"], np.int32),
+                  parents=dev(x["parents"], np.int32))
+    t = dict(q=dev(w.q, np.uint16), kv=dev(x["kv_buf"], np.uint16),
+             kv_indices=torch.full((w.kv_indices.size,), SENT_I32, dtype=torch.int32, device="cuda"),
+             kv_indptr=torch.full((B + 1,), SENT_I32, dtype=torch.int32, device="cuda"),
+             qo_indptr=dev(w.qo_indptr, np.int32),
+             mask=torch.full((w.mask.size,), SENT_U8, dtype=torch.uint8, device="cuda"),
+             mask_indptr=torch.full((B + 1,), SENT_I32, dtype=torch.int32, device="cuda"))
+    g = GpuCall(w, out_f32=True, tensors=t)
+    ap = tv.make_append_problem(B, w.max_q_len, w.max_kv_len, w.total_q, w.num_slots,
+                                int(x["prefix_indices"].size), int(w.kv_indices.size),
+                                int(w.mask.size))
+
+    def step(stream):
+        tv.append_draft(ap, pieces["draft_kv"], pieces["out_cache_loc"], pieces["prefix_indices"],
+                        pieces["prefix_indptr"], t["qo_indptr"], pieces["parents"], t["kv"],
+                        t["kv_indices"], t["kv_indptr"], t["mask"], t["mask_indptr"],
+                        stream=stream)
+        g.call(stream=stream)
+
+    step(None)
+    o, l = g.result()
+    ro, rl = oracle.run(w)
+    compare(o, l, ro, rl, bf16_out=False, label="eager append+verify")
+    eager = g.out_bits().copy()
+    eager_l = g.lse.cpu().numpy().copy()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        step(stream)
+    for rep in range(3):
+        g.out.fill_(0)
+        t["kv_indices"].fill_(SENT_I32)
+        t["mask"].fill_(SENT_U8)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(g.out_bits(), eager), rep
+        assert np.array_equal(g.lse.cpu().numpy(), eager_l), rep
+    # new draft rows: the replay writes them into the pool and attends to them
+    rng = np.random.default_rng(78)
+    new_rows = W.bf16_round(rng.standard_normal(x["draft_kv"].shape, dtype=np.float32))
+    pieces["draft_kv"].copy_(torch.from_numpy(new_rows.view(np.int16)).cuda())
+    graph.replay()
+    torch.cuda.synchronize()
+    kv2 = w.kv.copy()
+    kv2[x["out_cache_loc"]] = new_rows
+    import dataclasses
+    w2 = dataclasses.replace(w, kv=kv2)
+    o, l = g.result()
+    ro, rl = oracle.run(w2)
+    compare(o, l, ro, rl, bf16_out=False, label="replay with new draft rows")
