@@ -260,8 +260,9 @@ def append_times(w, steps, prefix_visible):
 
 def calibration():
     """Achievable peaks on this GPU, for context beside the published ones: a
-    1 GiB device-to-device copy (HBM read + write) and an 8192^3 bf16 matrix
-    product from torch (library code, not this path), each the median of 10."""
+    1 GiB device-to-device copy (HBM read + write), a 1 GiB sum (read), and an
+    8192^3 bf16 matrix product, all torch library code (not this path), each
+    the median of 10."""
     import torch
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -286,13 +287,50 @@ def calibration():
         return float(np.median(ts))
 
     t_copy = med(lambda: dst.copy_(src))
+    red = torch.empty((), dtype=torch.float32, device="cuda")
+    src_f = src.view(torch.float32)
+    t_read = med(lambda: torch.sum(src_f, dim=0, out=red))
     t_mm = med(lambda: torch.mm(a, bm, out=c))
-    res = {"copy_GBs": 2 * nbytes / t_copy / 1e9,
+    res = {"copy_GBs": 2 * nbytes / t_copy / 1e9, "read_GBs": nbytes / t_read / 1e9,
            "bf16_mm_TFLOPs": 2.0 * n ** 3 / t_mm / 1e12,
-           "how": "median of 10: 1 GiB device copy (read + write bytes); torch.mm bf16 8192^3"}
-    del src, dst, a, bm, c
+           "how": "median of 10: 1 GiB device copy (read + write bytes); torch.sum over "
+                  "1 GiB of fp32 (read); torch.mm bf16 8192^3"}
+    del src, dst, a, bm, c, red, src_f
     torch.cuda.synchronize()
     return res
+
+
+def gather_calibration(kv, kv_indices, reps=10):
+    """The same random 1152-byte pool rows gathered by library code
+    (torch.index_select into a dense copy), warm and after a cache scrub: what
+    plain row gathers reach on this GPU for this workload's slot pattern.
+    Rates count the gathered bytes read (the copy also writes as many)."""
+    import torch
+    idx = kv_indices.long()
+    out = torch.empty((idx.numel(), kv.shape[1]), dtype=kv.dtype, device="cuda")
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+    nbytes = idx.numel() * kv.shape[1] * kv.element_size()
+
+    def timed(cold):
+        ts = []
+        for i in range(reps + 2):
+            if cold:
+                scrub.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.index_select(kv, 0, idx, out=out)
+            e1.record()
+            e1.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    tw, tc = timed(False), timed(True)
+    del out, scrub
+    torch.cuda.synchronize()
+    return {"bytes_read": nbytes, "warm_us": tw * 1e6, "warm_read_GBs": nbytes / tw / 1e9,
+            "cold_us": tc * 1e6, "cold_read_GBs": nbytes / tc / 1e9,
+            "how": "torch.index_select of the workload's kv_indices rows, median of %d" % reps}
 
 
 SCRUB_BYTES = 1 << 30  # larger than the 256 MB MALL plus every XCD's L2
@@ -490,6 +528,8 @@ def main():
     cold = cold_cache_times(call, stream, args.cold_calls) if args.cold_calls > 0 else None
     append = append_times(w, args.steps, args.prefix_visible) if args.append else None
     calib = calibration() if not args.no_calibration else None
+    if calib:
+        calib["index_select_gather"] = gather_calibration(t["kv"], t["kv_indices"])
 
     kv_bytes, total_bytes, flops = algorithmic(w)
     us_per_call = ms_per_step * 1e3

@@ -438,3 +438,60 @@ def test_causal_chain_verify(ns):
     w = W.chain(402, [3000, 17], 12, num_heads=16)
     full_check(w, num_splits=ns, out_f32=True, label="chain ns=%d" % ns)
     full_check(W.prefix_visible_form(w), num_splits=ns, label="chain pv ns=%d" % ns)
+
+
+# ------------------------------------- guard bands and replays with new lengths
+
+@pytest.mark.parametrize("ns", [1, 3])
+def test_rows_outside_requests_are_untouched(ns):
+    """q rows before the first request and after the last belong to no request:
+    their out and lse entries keep whatever they held (NaN canaries here)."""
+    print("guard rows ns=%d" % ns, flush=True)
+    import dataclasses
+    w = W.small(601, [200, 40], [5, 3], num_heads=8)
+    rng = np.random.default_rng(601)
+    front = W.bf16_round(rng.standard_normal((3, 8, 576), dtype=np.float32))
+    back = W.bf16_round(rng.standard_normal((5, 8, 576), dtype=np.float32))
+    w2 = dataclasses.replace(w, q=np.concatenate([front, w.q, back]),
+                             qo_indptr=(w.qo_indptr + 3).astype(np.int32))
+    for out_f32 in (False, True):
+        g = GpuCall(w2, num_splits=ns, out_f32=out_f32)
+        g.call()
+        o, l = g.result()
+        inside = slice(3, 3 + w.total_q)
+        assert np.all(np.isnan(o[:3])) and np.all(np.isnan(o[inside.stop:]))
+        assert np.all(np.isnan(l[:3])) and np.all(np.isnan(l[inside.stop:]))
+        ro, rl = oracle.run(w)
+        compare(o[inside], l[inside], ro, rl, bf16_out=not out_f32, label="guard ns=%d" % ns)
+
+
+def test_graph_replay_follows_new_lengths_within_bounds():
+    """A captured call replays over device-side lengths that changed after the
+    capture (shorter prefixes, one request emptied), within the captured bounds."""
+    print("graph replay with new lengths", flush=True)
+    big = W.small(602, [3000, 1500, 700], [6, 6, 6], num_heads=8, pool=12000)
+    small = W.small(603, [900, 0, 2500], [6, 6, 6], num_heads=8, pool=12000)
+    g = GpuCall(big)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        g.call(stream=stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    o, l = g.result()
+    ro, rl = oracle.run(big)
+    compare(o, l, ro, rl, bf16_out=True, label="replay big")
+    # the new inputs go into the front of the same (larger) buffers
+    for k, v in (("q", small.q.view(np.int16)), ("kv", small.kv.view(np.int16)),
+                 ("kv_indices", small.kv_indices), ("kv_indptr", small.kv_indptr),
+                 ("qo_indptr", small.qo_indptr), ("mask", small.mask),
+                 ("mask_indptr", small.mask_indptr)):
+        src = torch.from_numpy(np.ascontiguousarray(v)).cuda().reshape(-1)
+        g.t[k].view(-1)[:src.numel()].copy_(src)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    o, l = g.result()
+    ro, rl = oracle.run(small)
+    compare(o, l, ro, rl, bf16_out=True, label="replay small")
