@@ -253,9 +253,13 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     // units share the reads (measured: at 72 rows x 205 splits it gains, at
     // 512 rows x 61 splits the extra workgroups cost more than they save)
     const bool sliced = gx * p->batch < 4 * kCUs && lay.plan.max_splits > 64;
-    if (tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, sliced, s) !=
-        hipSuccess)
-      return TV_ERR_LAUNCH;
+    // few splits per row (batches of many requests): one wave per row, all of
+    // its splits in flight at once, instead of a workgroup per row
+    const hipError_t e =
+        lay.plan.max_splits <= tv::MERGE_WAVE_SPLITS
+            ? tv::launch_merge_rows(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, s)
+            : tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, sliced, s);
+    if (e != hipSuccess) return TV_ERR_LAUNCH;
   }
   return TV_OK;
 }

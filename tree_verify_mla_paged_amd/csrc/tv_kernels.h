@@ -124,5 +124,9 @@ hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent
 // merging a quarter of the value dims.
 hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
                         bool sliced, hipStream_t st);
+// Plans of at most MERGE_WAVE_SPLITS splits: one wave per row.
+constexpr int MERGE_WAVE_SPLITS = 16;
+hipError_t launch_merge_rows(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
+                             hipStream_t st);
 
 }  // namespace tv

@@ -160,6 +160,99 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   }
 }
 
+// Requests split at most MERGE_WAVE_SPLITS ways: one wave per row, four rows
+// per workgroup.  Lane s holds split s's lse (and scale exponent); every lane
+// owns 8 value dims and issues the loads of all the row's splits at once,
+// before the weights are known; the weights come from wave reductions, with no
+// LDS and no barrier.  Same arithmetic as tv_merge_kernel: M = max_s lse_s,
+// w_s = exp(lse_s - M), out = sum_s w_s 2^k_s h_s / sum_s w_s, lse = M + ln sum_s w_s.
+template <int OUT, bool F16P>
+__global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
+  constexpr int MS = MERGE_WAVE_SPLITS;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);  // wave-uniform
+  const int q0 = p.qo_indptr[b];
+  const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
+  if (r >= R) return;
+  const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
+  const int ns = min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, MS);
+  if (ns <= 1) return;  // written directly by the split kernel
+  const int64_t g = (int64_t)q0 * p.num_heads + r;
+  const int LS = F16P ? 2 : 1;
+  const float* ls = p.ws_lse + g * p.max_splits * LS;
+  const int d = lane * 8;
+  f16x8 vh[MS];
+  f32x4 v0[MS], v1[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s < ns) {
+      if (F16P) {
+        vh[s] = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.ws_o) +
+                                                (g * p.max_splits + s) * VD + d);
+      } else {
+        const float* po = static_cast<const float*>(p.ws_o) + (g * p.max_splits + s) * VD + d;
+        v0[s] = *reinterpret_cast<const f32x4*>(po);
+        v1[s] = *reinterpret_cast<const f32x4*>(po + 4);
+      }
+    }
+  }
+  const float lv = lane < ns ? ls[LS * lane] : -INFINITY;
+  const float kx = (F16P && lane < ns) ? ls[LS * lane + 1] : 0.f;
+  float M = lv;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float lse = -INFINITY;
+  if (M != -INFINITY) {  // uniform
+    const float w = __expf(lv - M);  // exp(-inf) = 0 for lanes past ns and empty splits
+    float W = w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) W += __shfl_xor(W, o);
+    const float wn = F16P ? __builtin_ldexpf(w, (int)kx) : w;
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      if (s < ns) {
+        const float ws = __shfl(wn, s);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] += ws * (F16P ? (float)vh[s][e] : (e < 4 ? v0[s][e] : v1[s][e - 4]));
+      }
+    }
+    const float inv = 1.f / W;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    lse = M + logf(W);
+  }
+  if (lane == 0) p.lse[g] = lse;
+  if (OUT == OUT_F32) {
+    float* o = static_cast<float*>(p.out) + g * VD + d;
+    *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[e];
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + g * VD + d) = o;
+  }
+}
+
+hipError_t launch_merge_rows(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
+                             hipStream_t st) {
+  MergeParams a = p;
+  void* args[] = {&a};
+  static const void* const fns[2][2] = {
+      {reinterpret_cast<const void*>(&tv_merge_rows_kernel<OUT_BF16, false>),
+       reinterpret_cast<const void*>(&tv_merge_rows_kernel<OUT_BF16, true>)},
+      {reinterpret_cast<const void*>(&tv_merge_rows_kernel<OUT_F32, false>),
+       reinterpret_cast<const void*>(&tv_merge_rows_kernel<OUT_F32, true>)}};
+  const int wpg = NT / 64;
+  return hipLaunchKernel(fns[out == OUT_F32][f16_parts], dim3((rows + wpg - 1) / wpg, batch),
+                         dim3(NT), args, 0, st);
+}
+
 hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
                         bool sliced, hipStream_t st) {
   MergeParams a = p;
