@@ -256,7 +256,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
     // few splits per row (batches of many requests): one wave per row, all of
     // its splits in flight at once, instead of a workgroup per row
     const hipError_t e =
-        lay.plan.max_splits <= tv::MERGE_WAVE_SPLITS
+        lay.plan.max_splits <= tv::merge_wave_splits(!sp.precise)
             ? tv::launch_merge_rows(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, s)
             : tv::launch_merge(mp, (int)gx, p->batch, p->out_dtype, !sp.precise, sliced, s);
     if (e != hipSuccess) return TV_ERR_LAUNCH;

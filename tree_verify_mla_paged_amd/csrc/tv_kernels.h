@@ -124,8 +124,9 @@ hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent
 // merging a quarter of the value dims.
 hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
                         bool sliced, hipStream_t st);
-// Plans of at most MERGE_WAVE_SPLITS splits: one wave per row.
-constexpr int MERGE_WAVE_SPLITS = 16;
+// Plans of at most merge_wave_splits splits: one wave per row, every split's
+// partial held in registers (32 fp16 or 16 fp32 partial rows per lane).
+constexpr int merge_wave_splits(bool f16_parts) { return f16_parts ? 32 : 16; }
 hipError_t launch_merge_rows(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
                              hipStream_t st);
 

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   }
 }
 
-// Requests split at most MERGE_WAVE_SPLITS ways: one wave per row, four rows
+// Requests split at most merge_wave_splits(F16P) ways: one wave per row, four rows
 // per workgroup.  Lane s holds split s's lse (and scale exponent); every lane
 // owns 8 value dims and issues the loads of all the row's splits at once,
 // before the weights are known; the weights come from wave reductions, with no
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
 // w_s = exp(lse_s - M), out = sum_s w_s 2^k_s h_s / sum_s w_s, lse = M + ln sum_s w_s.
 template <int OUT, bool F16P>
 __global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
-  constexpr int MS = MERGE_WAVE_SPLITS;
+  constexpr int MS = merge_wave_splits(F16P);
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);  // wave-uniform
