@@ -524,6 +524,19 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
+    # each replay bracketed by its own events (outside the graph, on its stream)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(50)]
+    with torch.cuda.stream(stream):
+        for a, b in gev:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+    torch.cuda.synchronize()
+    gus = np.array([a.elapsed_time(b) * 1e3 for a, b in gev])
+    graph_events = {"replays": len(gev), "median_us": float(np.median(gus)),
+                    "p10_us": float(np.percentile(gus, 10)),
+                    "p90_us": float(np.percentile(gus, 90))}
 
     cold = cold_cache_times(call, stream, args.cold_calls) if args.cold_calls > 0 else None
     append = append_times(w, args.steps, args.prefix_visible) if args.append else None
@@ -564,6 +577,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, bf16-rounded N(0,1))",
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "graph_us_per_call": graph_us,
+        "graph_replay_events": graph_events,
         "cold_cache": cold,
         "append_draft": append,
         "calibration": calib,
