@@ -115,6 +115,18 @@ def test_plan_heuristic_fills_the_chip():
     assert tv.workspace_bytes(p) >= 32 * pl["max_splits"] * 12 * 4
 
 
+def test_no_dispatch_order_when_every_work_item_has_a_compute_unit():
+    """8 requests of 128 rows, keys up to 3968: at most 256 work items, all
+    resident at once, so no longest-first order (and no pack launch)."""
+    p = prob(batch=8, num_heads=8, total_q=128, max_q_len=16, max_kv_len=3968,
+             total_kv=18600, total_mask=16 * 18600, num_slots=65536)
+    pl = tv.plan(p)
+    assert 8 * pl["max_splits"] * pl["row_blocks"] <= 256 and pl["merge"]
+    prow = 128 * 8 * pl["max_splits"]
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert pl["workspace_bytes"] == align(prow * 1024) + align(prow * 8)
+
+
 def test_bad_shapes_are_rejected():
     for kw in [dict(num_heads=0), dict(batch=-1), dict(max_kv_len=-1), dict(num_splits=-2),
                dict(total_kv=2 ** 31), dict(max_q_len=10, total_q=9)]:

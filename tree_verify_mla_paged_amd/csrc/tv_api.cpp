@@ -132,8 +132,10 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
     off += lay->wsl_bytes;
   }
   // requests of unequal lengths: a longest-first dispatch order (written by the
-  // pack kernel) balances the compute units
-  if (p->batch > 1 && L > 0 && total_work <= tv::SCHED_MAX_WORK) {
+  // pack kernel) balances the compute units.  Not when every work item has a
+  // compute unit of its own (one workgroup fits per unit): they all start at
+  // once, and the order would only cost a launch
+  if (p->batch > 1 && L > 0 && total_work > kCUs && total_work <= tv::SCHED_MAX_WORK) {
     lay->order_off = off;
     lay->order_bytes = align256(total_work * 4);
     off += lay->order_bytes;
