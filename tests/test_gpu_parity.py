@@ -495,3 +495,42 @@ def test_graph_replay_follows_new_lengths_within_bounds():
     o, l = g.result()
     ro, rl = oracle.run(small)
     compare(o, l, ro, rl, bf16_out=True, label="replay small")
+
+
+# ------------------------------------------------- pools beyond 4 GiB
+
+WIDE_SLOTS = 4_200_000  # 4.84 GB of 1152-byte rows: gathers take 64-bit addresses
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("H", [8, 3])  # mask bytes read in the loop / packed words
+def test_pool_beyond_4gib_gives_the_same_bits(flags, H):
+    """The same keys moved to the top of a pool larger than 4 GiB (the slot
+    offsets no longer fit 32 bits, so the gathers use 64-bit addresses) give
+    bit-identical outputs; the rest of the big pool is NaN."""
+    print("pool beyond 4 GiB flags=%d H=%d" % (flags, H), flush=True)
+    assert WIDE_SLOTS * 1152 > 2 ** 32
+    w = W.small(701, [900, 37, 2500], [7, 3, 12], num_heads=H)
+    g = GpuCall(w, num_splits=3, out_f32=True, flags=flags)
+    g.call()
+    narrow = g.out_bits().copy()
+    narrow_l = g.lse.cpu().numpy().copy()
+    offset = WIDE_SLOTS - w.num_slots
+    big = torch.full((WIDE_SLOTS, 576), 0x7FC0, dtype=torch.int16, device="cuda")
+    big[offset:].copy_(g.t["kv"])
+    idx = (g.t["kv_indices"].long() + offset).to(torch.int32)
+    p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, WIDE_SLOTS,
+                        int(w.kv_indices.size), int(w.mask.size), 3, tv.OUT_F32, flags)
+    out = torch.full_like(g.out, float("nan"))
+    lse = torch.full_like(g.lse, float("nan"))
+    ws = torch.empty(max(tv.workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    tv.verify_attn(p, g.t["q"], big, idx, g.t["kv_indptr"], g.t["qo_indptr"], g.t["mask"],
+                   g.t["mask_indptr"], float(w.sm_scale), out, lse, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int32).cpu().numpy(), narrow)
+    assert np.array_equal(lse.cpu().numpy().view(np.int32), narrow_l.view(np.int32))
+    o, l = g.result()
+    ro, rl = oracle.run(w)
+    compare(o, l, ro, rl, bf16_out=False, label="wide flags=%d" % flags)
+    del big
+    torch.cuda.empty_cache()
