@@ -534,3 +534,32 @@ def test_pool_beyond_4gib_gives_the_same_bits(flags, H):
     compare(o, l, ro, rl, bf16_out=False, label="wide flags=%d" % flags)
     del big
     torch.cuda.empty_cache()
+
+
+def test_timed_entry_point_matches_and_stamps_events():
+    """tv_verify_attn_timed runs the same kernels (same bits) and stamps the two
+    events with the split kernel's own dispatch: a positive duration."""
+    print("timed entry point", flush=True)
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from bench import HipEvents
+    w = W.config(2)
+    g = GpuCall(w, out_f32=True)
+    g.call()
+    ref = g.out_bits().copy()
+    ref_l = g.lse.cpu().numpy().copy()
+    g.out.fill_(0)
+    ev = HipEvents()
+    a, b = ev.create(), ev.create()
+    t = g.t
+    tv.verify_attn_timed(g.p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                         t["mask"], t["mask_indptr"], float(w.sm_scale), g.out, g.lse, g.ws,
+                         g.ws.numel(), a, b)
+    ms = ev.elapsed_ms(a, b)
+    torch.cuda.synchronize()
+    ev.destroy(a)
+    ev.destroy(b)
+    assert np.array_equal(g.out_bits(), ref)
+    assert np.array_equal(g.lse.cpu().numpy(), ref_l)
+    assert 0.0 < ms < 100.0, ms
