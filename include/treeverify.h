@@ -81,7 +81,7 @@ typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
 /* Host-side description of one call.  Device-side lengths may vary between
  * calls (or graph replays) as long as they stay within these bounds. */
 typedef struct tv_problem {
-  int32_t batch;      /* B >= 0 requests                                             */
+  int32_t batch;      /* 0 <= B <= 65535 requests                                    */
   int32_t num_heads;  /* H >= 1 query heads sharing one latent KV head               */
   int64_t total_q;    /* rows of q / out / lse (draft tokens), >= qo_indptr[B]       */
   int32_t max_q_len;  /* >= every n_b = qo_indptr[b+1] - qo_indptr[b]                */
@@ -218,7 +218,7 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
  * tv_verify_attn takes.  Capture-safe: two kernel launches on `stream`.
  */
 typedef struct tv_append_problem {
-  int32_t batch;        /* B >= 0                                                    */
+  int32_t batch;        /* 0 <= B <= 65535                                           */
   int32_t max_q_len;    /* >= every n_b                                             */
   int32_t max_kv_len;   /* >= every P_b + n_b                                       */
   int32_t flags;        /* TV_FLAG_PREFIX_VISIBLE or 0; other bits TV_ERR_UNSUPPORTED */

@@ -128,7 +128,8 @@ def test_no_dispatch_order_when_every_work_item_has_a_compute_unit():
 
 
 def test_bad_shapes_are_rejected():
-    for kw in [dict(num_heads=0), dict(batch=-1), dict(max_kv_len=-1), dict(num_splits=-2),
+    for kw in [dict(num_heads=0), dict(batch=-1), dict(batch=65536), dict(max_kv_len=-1),
+               dict(num_splits=-2),
                dict(total_kv=2 ** 31), dict(max_q_len=10, total_q=9)]:
         assert tv.workspace_bytes(prob(**kw)) == 0
         with pytest.raises(tv.TreeVerifyError) as e:
@@ -227,7 +228,8 @@ def test_append_draft_argument_errors_before_any_launch():
     fake = 1 << 20  # aligned non-null stand-in; never dereferenced on these paths
     args = [fake] * 11  # draft_kv .. mask_indptr
     # sizes
-    for kw, code in [(dict(batch=-1), 2), (dict(total_kv=2 ** 31), 2), (dict(max_q_len=40), 2),
+    for kw, code in [(dict(batch=-1), 2), (dict(batch=65536), 2), (dict(total_kv=2 ** 31), 2),
+                     (dict(max_q_len=40), 2),
                      (dict(max_kv_len=1 << 30, max_q_len=9), 2), (dict(flags=1), 4),
                      (dict(flags=8), 4)]:
         assert tv.append_draft_status(aprob(**kw), *args) == code, kw

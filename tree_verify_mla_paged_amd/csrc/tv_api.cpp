@@ -36,6 +36,7 @@ namespace {
 constexpr int64_t kMaxInt32 = 2147483647;
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kMinSplitTiles = 4;  // keys per split >= 128 unless the caller asks otherwise
+constexpr int kMaxGridY = 65535;   // largest grid y dimension of a launch
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -79,6 +80,8 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   if ((p->flags & ~(TV_FLAG_PRECISE_P | TV_FLAG_PREFIX_VISIBLE)) != 0 || p->reserved != 0)
     return TV_ERR_UNSUPPORTED;
   if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
+  // the pack and merge grids put the request in their y dimension
+  if (p->batch > kMaxGridY) return TV_ERR_SHAPE;
   // per-request key offsets are 32-bit byte offsets (4 * key) in the kernels
   if (p->max_kv_len >= (1 << 30)) return TV_ERR_SHAPE;
   if ((int64_t)p->max_q_len * p->num_heads > kMaxInt32 ||
@@ -363,7 +366,7 @@ tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
   if ((p->flags & ~TV_FLAG_PREFIX_VISIBLE) != 0) return TV_ERR_UNSUPPORTED;
   if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->total_prefix > kMaxInt32 ||
       p->total_q > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL || p->max_q_len > p->max_kv_len ||
-      p->max_kv_len >= (1 << 30) || p->batch >= (1 << 16))
+      p->max_kv_len >= (1 << 30) || p->batch > kMaxGridY)
     return TV_ERR_SHAPE;
   if (p->batch == 0) return TV_OK;
   if (!prefix_indptr || !qo_indptr || !kv_indptr) return TV_ERR_NULL;
