@@ -110,21 +110,41 @@ def algorithmic(w):
 
 
 def source_hash():
+    """The split kernel's source and the parameter structs it is launched with."""
     h = hashlib.sha256()
-    for f in ("tv_split.hip", "tv_kernels.h", "tv_api.cpp"):
+    for f in ("tv_split.hip", "tv_kernels.h"):
         h.update(open(os.path.join(ROOT, "tree_verify_mla_paged_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: str, splits: int, precise: bool):
+def plan_for(args):
+    """The library's launch plan for the benchmark configuration."""
+    import tree_verify_mla_paged_amd as tv
+    w, _, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
+    splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
+    p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
+                        int(w.kv_indices.size), int(w.mask.size), splits,
+                        tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
+                        (tv.FLAG_PRECISE_P if args.precise else 0) |
+                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
+    return launch_shape(tv.plan(p))
+
+
+def launch_shape(plan: dict) -> dict:
+    """The part of a plan that fixes the split kernel's launch and traffic."""
+    return {k: plan[k] for k in ("split_keys", "max_splits", "row_blocks")}
+
+
+def measured_traffic(cfg: str, splits: int, precise: bool, plan: dict):
     """HBM bytes per split-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current split-kernel source with the same
+    launch plan; else None."""
     path = os.path.join(ROOT, "profiles", "split_kernel_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
     e = d.get("workloads", {}).get("%s/splits=%d/precise=%d" % (cfg, splits, int(precise)))
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash() or e.get("plan") != plan:
         return None
     return e.get("bytes_per_launch")
 
@@ -199,6 +219,7 @@ def write_traffic(args):
     key = "%s/splits=%d/precise=%d" % (args.config, splits, int(args.precise))
     d.setdefault("workloads", {})[key] = {
         "source_hash": source_hash(),
+        "plan": plan_for(args),
         "commands": ["rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o fetch -- python3 bench.py "
                      "--config %s --splits %d%s --counter-workload %d" % (
                          args.config, splits, " --precise" if args.precise else "", 10),
@@ -559,7 +580,8 @@ def main():
                 "frac": achieved / HBM_PEAK_GBS}
     # the counter summary covers the full mask form only
     roof["traffic"] = (None if args.prefix_visible else
-                       measured_traffic(args.config, splits, bool(args.precise)))
+                       measured_traffic(args.config, splits, bool(args.precise),
+                                        launch_shape(plan)))
     roof["kernel"] = "tv_split_kernel"
     roof["kernel_avg_us"] = split_avg_ms * 1e3
     roof["kernel_timed_launches"] = len(split_ms)
