@@ -563,3 +563,25 @@ def test_timed_entry_point_matches_and_stamps_events():
     assert np.array_equal(g.out_bits(), ref)
     assert np.array_equal(g.lse.cpu().numpy(), ref_l)
     assert 0.0 < ms < 100.0, ms
+
+
+def test_marshaling_bug_runs_but_answers_the_wrong_question():
+    """The pages' failure: the draft slots left out of kv_indices (21 keys, not
+    30) and the mask at the prefix-only stride (9 x 21).  Such inputs are
+    well-formed, so the call runs and matches the oracle on those same inputs,
+    but its output is far from the correct inputs' (mean relative error 0.24
+    on this seeded workload against the 2e-3 bar)."""
+    print("marshaling bug symptom", flush=True)
+    import dataclasses
+    w = W.config(1)
+    bad = dataclasses.replace(w, kv_indices=w.kv_indices[:21].copy(),
+                              kv_indptr=np.array([0, 21], np.int32),
+                              mask=np.ones(9 * 21, np.uint8),
+                              mask_indptr=np.array([0, 189], np.int32))
+    o, l = run(bad, out_f32=True)
+    rb, lb = oracle.run(bad)
+    compare(o, l, rb, lb, bf16_out=False, label="bad inputs, same oracle")
+    ro, rl = oracle.run(w)
+    rel = float(np.abs(o - ro).sum() / np.abs(ro).sum())
+    print("   relative error against the correct inputs: %.3f" % rel, flush=True)
+    assert rel > 0.1
