@@ -121,8 +121,9 @@ tv_status tv_get_plan(const tv_problem* p, tv_plan* plan);
  *  - when more than one split is used, the per-split partial outputs:
  *    total_q * H * max_splits entries of 512 fp16 values plus two fp32 (lse,
  *    scale exponent), or with TV_FLAG_PRECISE_P of 512 + 1 fp32;
- *  - for a batch of more than one request, one int32 per work item (the
- *    longest-first dispatch order). */
+ *  - for a batch of more than one request whose launch has more than 256
+ *    work items (request x split x 128-row block), one int32 per work item
+ *    (the longest-first dispatch order). */
 size_t tv_workspace_bytes(const tv_problem* p);
 
 /*
