@@ -214,3 +214,19 @@ def test_append_and_verify_captured_in_one_graph():
     o, l = g.result()
     ro, rl = oracle.run(w2)
     compare(o, l, ro, rl, bf16_out=False, label="replay with new draft rows")
+
+
+def test_append_many_requests_carries_across_scan_chunks():
+    """3000 requests: the indptr scan runs over twelve 256-request chunks, each
+    carrying the running totals of the ones before."""
+    print("append 3000 requests", flush=True)
+    rng = np.random.default_rng(504)
+    prefix = [int(x) for x in rng.integers(0, 40, size=3000)]
+    drafts = [int(x) for x in rng.integers(0, 4, size=3000)]
+    w = W.small(504, prefix, drafts, 1, max_branch=2)
+    for pv in (False, True):
+        x, pool, ki, kp, m, mp = gpu_append(w, prefix_visible=pv, guard=0)
+        ekv, eki, ekp, em, emp = expected(x, pv)
+        assert np.array_equal(kp, ekp) and np.array_equal(mp, emp)
+        assert np.array_equal(ki, eki) and np.array_equal(m, em)
+        assert np.array_equal(pool, ekv)

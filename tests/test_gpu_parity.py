@@ -585,3 +585,15 @@ def test_marshaling_bug_runs_but_answers_the_wrong_question():
     rel = float(np.abs(o - ro).sum() / np.abs(ro).sum())
     print("   relative error against the correct inputs: %.3f" % rel, flush=True)
     assert rel > 0.1
+
+
+def test_many_tiny_requests():
+    """3000 requests of 0-3 drafts after 0-40 prefix keys: a 3000-row grid y,
+    and a longest-first order over 3000 work items."""
+    print("3000 tiny requests", flush=True)
+    rng = np.random.default_rng(605)
+    prefix = [int(x) for x in rng.integers(0, 40, size=3000)]
+    drafts = [int(x) for x in rng.integers(0, 4, size=3000)]
+    w = W.small(605, prefix, drafts, 8, max_branch=2)
+    full_check(w, out_f32=True, label="3000 requests")
+    full_check(w, num_splits=2, label="3000 requests, 2 splits")
