@@ -597,3 +597,36 @@ def test_many_tiny_requests():
     w = W.small(605, prefix, drafts, 8, max_branch=2)
     full_check(w, out_f32=True, label="3000 requests")
     full_check(w, num_splits=2, label="3000 requests, 2 splits")
+
+
+@pytest.mark.parametrize("H", [7, 9, 10, 11, 12])
+def test_heads_around_the_mask_byte_threshold(H):
+    """Waves of 32 rows span at most 4 drafts for H = 8, 10 and 11 and up (the
+    split kernel reads the mask bytes, two drafts per load), more for H = 7 and
+    9 (packed words): 13 drafts put every residue of a wave's first row in play."""
+    print("heads around the mask-byte threshold H=%d" % H, flush=True)
+    w = W.small(606 + H, [150, 9], [13, 6], num_heads=H)
+    rng = np.random.default_rng(606 + H)
+    w.mask[:] = (rng.random(w.mask.size) < 0.6).astype(np.uint8)
+    for ns in (1, 3):
+        full_check(w, num_splits=ns, out_f32=True, label="H=%d ns=%d" % (H, ns))
+
+
+def test_batch_beyond_the_ordered_grid_limit():
+    """400 requests x 44 one-tile splits x 4 row blocks (4 drafts x 128 heads)
+    = 70400 work items, above the longest-first order's 65536: the natural
+    dispatch order; with more than 32 splits the merge is the workgroup-per-row
+    one."""
+    print("70400 work items", flush=True)
+    rng = np.random.default_rng(607)
+    prefix = [int(x) for x in rng.integers(1270, 1390, size=400)]
+    w = W.small(607, prefix, [4] * 400, 128, pool=600_000)
+    import tree_verify_mla_paged_amd as tvm
+    from gpu_util import problem_for
+    pl = tvm.plan(problem_for(w, num_splits=44))
+    assert 400 * pl["max_splits"] * pl["row_blocks"] > 65536 and pl["max_splits"] > 32
+    rows = sample_rows(w, 200, seed=607)
+    ro, rl = oracle.run(w, rows=rows)
+    o, l = run(w, num_splits=44, out_f32=True)
+    compare(o.reshape(-1, 512)[rows], l.reshape(-1)[rows], ro, rl, bf16_out=False,
+            label="70400 work items")
