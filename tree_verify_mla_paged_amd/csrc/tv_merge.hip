@@ -60,7 +60,9 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   const int slice = blockIdx.x % DS;
   if (r >= R) return;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
-  const int ns = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
+  // (clamped to the plan: a request longer than max_kv_len breaks the
+  // preconditions, and then reads stay inside the row's partials)
+  const int ns = min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, p.max_splits);
   if (ns <= 1) return;  // written directly by the split kernel
   const int64_t g = (int64_t)q0 * p.num_heads + r;
   const int LS = F16P ? 2 : 1;  // floats per (row, split) in ws_lse
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
   const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
   if (r >= R) return;
   const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
-  const int ns = min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, MS);
+  const int ns = min(min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, MS), p.max_splits);
   if (ns <= 1) return;  // written directly by the split kernel
   const int64_t g = (int64_t)q0 * p.num_heads + r;
   const int LS = F16P ? 2 : 1;
