@@ -2,22 +2,22 @@
 """Benchmark of tree-masked verify attention on one MI355X.
 
 One step = one tv_verify_attn call (mask packing + split attention + LSE merge)
-over one batch of seeded synthetic inputs already resident in HBM.  The timed
-steps are `steps` calls enqueued back to back on one stream.  Every
-TIMING_STRIDE-th of them carries a HIP event pair that the split-attention
-kernel's own dispatch stamps with its start and end (tv_verify_attn_timed); the
-others carry none, since event handling adds several microseconds to a call.
-The same call replayed from a captured HIP graph is timed separately and
-reported beside it (events inside a captured graph cannot be timed on this
-runtime).  Default workload: 1 request, 32
-draft tokens, 32768-key prefix, 16 heads (the 32k-prefix configuration the
-metric is quoted at), with the library's own split plan (`--splits 32` gives
-the configuration's literal split count; outputs do not depend on it).
+over one batch of seeded synthetic inputs already resident in HBM, with cold
+caches: before each step a 1 GiB fill kernel (outside the timed events) evicts
+the pool, indices and mask from the 256 MB MALL and the L2s.  Each timed step's
+call is bracketed by events on its stream, and its split-attention kernel's own
+dispatch stamps a second event pair with its start and end
+(tv_verify_attn_timed).  The warm-up steps are the same, untimed.  Beside it:
+the same call back to back with warm caches, and replayed from a captured HIP
+graph.  Default workload: 1 request, 32 draft tokens, 32768-key prefix, 16
+heads (the 32k-prefix configuration the metric is quoted at), with the
+library's own split plan (`--splits 32` gives the configuration's literal
+split count; outputs do not depend on it).
 
 Prints one JSON line: throughput as gathered-KV GB/s (sum over requests of
-L_b * 1152 bytes per call / call time), the roofline of the split kernel from
-its event-timed average over the sampled timed steps, and the fp64 CPU oracle timed on
-a bounded sample.
+L_b * 1152 bytes per call / median cold call time), the roofline of the split
+kernel from its event-timed average over the timed steps, and the fp64 CPU
+oracle timed on a bounded sample.
 """
 import argparse
 import ctypes
@@ -31,8 +31,9 @@ import time
 import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# every TIMING_STRIDE-th timed step carries the split kernel's event pair
-TIMING_STRIDE = 8
+# every WARM_STRIDE-th call of the warm back-to-back figure carries the split
+# kernel's event pair (every timed, cold-cache step carries one)
+WARM_STRIDE = 8
 sys.path.insert(0, ROOT)
 
 import tv_workload as W  # noqa: E402
@@ -357,35 +358,60 @@ def gather_calibration(kv, kv_indices, reps=10):
 SCRUB_BYTES = 1 << 30  # larger than the 256 MB MALL plus every XCD's L2
 
 
-def cold_cache_times(call, stream, n):
-    """Whole-call time with cold caches: before each call a 1 GiB fill kernel
-    evicts the pool, the indices and the mask from the MALL and the L2s.  The
-    events bracket the call only, on its own stream.  The same bracketing of
-    back-to-back calls without the fill gives the warm figure measured the
-    same way (event handling adds a few microseconds to each)."""
+def warm_times(call, ev, stream, n):
+    """Secondary figure: n calls back to back on one stream (caches warm: the
+    pool partly stays in the MALL between calls), wall clock over the n calls;
+    every WARM_STRIDE-th call's split kernel stamps an event pair (event
+    handling adds a few microseconds to a call, so the others carry none)."""
     import torch
-    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
-
-    def timed(with_scrub):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        with torch.cuda.stream(stream):
-            for i in range(n):
-                if with_scrub:
-                    scrub.fill_(i & 0xFF)
-                evs[i][0].record(stream)
-                call()
-                evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-        return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
-                "p90_us": float(np.percentile(us, 90))}
-
-    timed(True)  # first pass: allocator and fill kernel warm-up
-    res = {"calls": n, "scrub_bytes": SCRUB_BYTES, "cold": timed(True), "warm": timed(False)}
-    del scrub
+    pairs = [(ev.create(), ev.create()) for _ in range(0, n, WARM_STRIDE)]
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            call()
     torch.cuda.synchronize()
-    return res
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            call(pairs[i // WARM_STRIDE] if i % WARM_STRIDE == 0 else None)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / n
+    split = [ev.elapsed_ms(a, b) * 1e3 for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    return {"calls": n, "us_per_call": us, "split_kernel_avg_us": float(np.mean(split)),
+            "split_kernel_timed_launches": len(split)}
+
+
+def graph_times(call, stream, n):
+    """The call captured into a HIP graph: wall clock over n replays back to
+    back, and 50 replays each bracketed by events outside the graph."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for _ in range(n):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - g0) * 1e6 / n
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(50)]
+    with torch.cuda.stream(stream):
+        for e0, e1 in gev:
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    gus = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in gev])
+    del graph
+    return graph_us, {"replays": len(gev), "median_us": float(np.median(gus)),
+                      "p10_us": float(np.percentile(gus, 10)),
+                      "p90_us": float(np.percentile(gus, 90))}
 
 
 def cpu_baseline(w, gpu_out, gpu_lse, kv_bytes, budget_s, out_f32):
@@ -459,8 +485,9 @@ def main():
     ap.add_argument("--precise", action="store_true",
                     help="probabilities as a bf16 hi + lo pair in the P.V product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-calls", type=int, default=30,
-                    help="calls timed with a cache scrub before each (0 = skip)")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="only the warm-up and timed (cold-cache) steps, no warm, graph or "
+                         "calibration runs: the command of the committed kernel traces")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--counter-workload", type=int, default=0, metavar="N",
                     help="run the calibration copy and N calls for rocprofv3 --pmc, no timing")
@@ -505,72 +532,65 @@ def main():
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.Stream()
     sid = int(stream.cuda_stream)
-
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(0, args.steps, TIMING_STRIDE)]
 
-    def call(i=None):
-        if i is None:
+    def call(pair=None):
+        if pair is None:
             tv.verify_attn(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
                            t["mask"], t["mask_indptr"], float(w.sm_scale), out, lse, ws,
                            ws.numel(), stream=sid)
         else:
             tv.verify_attn_timed(p, t["q"], t["kv"], t["kv_indices"], t["kv_indptr"],
                                  t["qo_indptr"], t["mask"], t["mask_indptr"], float(w.sm_scale),
-                                 out, lse, ws, ws.numel(), pairs[i][0], pairs[i][1], stream=sid)
+                                 out, lse, ws, ws.numel(), pair[0], pair[1], stream=sid)
 
+    # The timed steps: inputs resident in HBM, caches cold.  Before each step a
+    # 1 GiB fill kernel (outside the events, same stream) evicts the pool, the
+    # indices and the mask from the 256 MB MALL and the L2s.  Even steps are
+    # bracketed by events on the stream (the call time); odd steps carry
+    # instead the event pair that the split kernel's own dispatch stamps (the
+    # kernel time).  Each kind of event handling adds its own delay, so no step
+    # carries both.  The warm-up steps are the same, untimed.
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev)
+    n_call = (args.steps + 1) // 2
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps // 2)]
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_call)]
     with torch.cuda.stream(stream):
-        for _ in range(3):
+        for i in range(args.warmup):
+            scrub.fill_(i & 0xFF)
             call()
     torch.cuda.synchronize()
-    # warmup steps
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-
-    # the timed steps
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        call(i // TIMING_STRIDE if i % TIMING_STRIDE == 0 else None)
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            scrub.fill_((i + 1) & 0xFF)
+            if i % 2 == 0:
+                calls[i // 2][0].record(stream)
+                call()
+                calls[i // 2][1].record(stream)
+            else:
+                call(pairs[i // 2])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    split_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in calls])
+    split_ms = [ev.elapsed_ms(a, b) for a, b in pairs] or [float("nan")]
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
+    del scrub
     split_avg_ms = float(np.mean(split_ms))
+    ms_per_step = float(np.median(call_us)) * 1e-3
+    timed_region_s = t1 - t0
 
-    # the same call replayed from a captured graph (reported, not the metric)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        call()
-    torch.cuda.synchronize()
-    for _ in range(5):
-        graph.replay()
-    torch.cuda.synchronize()
-    g0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - g0) * 1e6 / args.steps
-    # each replay bracketed by its own events (outside the graph, on its stream)
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(50)]
-    with torch.cuda.stream(stream):
-        for a, b in gev:
-            a.record(stream)
-            graph.replay()
-            b.record(stream)
-    torch.cuda.synchronize()
-    gus = np.array([a.elapsed_time(b) * 1e3 for a, b in gev])
-    graph_events = {"replays": len(gev), "median_us": float(np.median(gus)),
-                    "p10_us": float(np.percentile(gus, 10)),
-                    "p90_us": float(np.percentile(gus, 90))}
+    warm = None
+    graph_us = graph_events = None
+    if not args.timed_only:
+        warm = warm_times(call, ev, stream, max(args.steps, 50))
+        graph_us, graph_events = graph_times(call, stream, max(args.steps, 50))
 
-    cold = cold_cache_times(call, stream, args.cold_calls) if args.cold_calls > 0 else None
     append = append_times(w, args.steps, args.prefix_visible) if args.append else None
-    calib = calibration() if not args.no_calibration else None
+    calib = calibration() if not (args.no_calibration or args.timed_only) else None
     if calib:
         calib["index_select_gather"] = gather_calibration(t["kv"], t["kv_indices"])
 
@@ -593,7 +613,15 @@ def main():
                                         launch_shape(plan)))
     roof["kernel"] = "tv_split_kernel"
     roof["kernel_avg_us"] = split_avg_ms * 1e3
-    roof["kernel_timed_launches"] = len(split_ms)
+    roof["kernel_timed_launches"] = len(pairs)
+    roof["timing"] = ("cold cache: the split kernel of every odd timed step, stamped by its own "
+                      "dispatch")
+    if warm:
+        # the same kernel with warm caches (back to back), for comparison
+        w_ach = (flops if roof["bound"] == "mfma" else total_bytes) / (
+            warm["split_kernel_avg_us"] * 1e-6) / (1e12 if roof["bound"] == "mfma" else 1e9)
+        roof["warm"] = {"kernel_avg_us": warm["split_kernel_avg_us"], "achieved": w_ach,
+                        "frac": w_ach / roof["peak"]}
     roof["algorithmic"] = {"bytes": total_bytes, "flops": flops,
                            "floor_us": max(t_hbm, t_mfma) * 1e6}
     if calib:
@@ -607,9 +635,18 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, bf16-rounded N(0,1))",
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "timing": ("value, ms_per_step and us_per_call: median over the even timed steps of "
+                   "the event-bracketed call, each step after a %d-byte cache scrub (cold MALL "
+                   "and L2); warm: back-to-back calls" % SCRUB_BYTES),
+        "timed_steps": {"calls_bracketed": len(calls), "median_us": float(np.median(call_us)),
+                        "p10_us": float(np.percentile(call_us, 10)),
+                        "p90_us": float(np.percentile(call_us, 90)),
+                        "mean_us": float(np.mean(call_us)),
+                        "wall_s": timed_region_s},
+        "warm": warm,
+        "warm_GBs": (kv_bytes / (warm["us_per_call"] * 1e-6) / 1e9) if warm else None,
         "graph_us_per_call": graph_us,
         "graph_replay_events": graph_events,
-        "cold_cache": cold,
         "append_draft": append,
         "calibration": calib,
         "floor_fraction": max(t_hbm, t_mfma) / (ms_per_step * 1e-3),

@@ -251,3 +251,74 @@ def test_append_draft_argument_errors_before_any_launch():
     a = list(args)
     a[0] = fake + 8
     assert tv.append_draft_status(aprob(), *a) == 2
+
+
+class _FakeDeviceTensor:
+    """Tensor metadata only (the binding's checks read nothing else)."""
+
+    def __init__(self, dtype, numel, contiguous=True, cuda=True):
+        import torch
+        self.dtype = dtype
+        self._n = numel
+        self._c = contiguous
+        self.is_cuda = cuda
+        self._es = torch.empty(0, dtype=dtype).element_size()
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._es
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("the checks must fail before any pointer is taken")
+
+
+def _args(p, **over):
+    import torch
+    rows = p.total_q * p.num_heads
+    a = dict(q=_FakeDeviceTensor(torch.bfloat16, rows * 576),
+             kv_buf=_FakeDeviceTensor(torch.bfloat16, p.num_slots * 576),
+             kv_indices=_FakeDeviceTensor(torch.int32, p.total_kv),
+             kv_indptr=_FakeDeviceTensor(torch.int32, p.batch + 1),
+             qo_indptr=_FakeDeviceTensor(torch.int32, p.batch + 1),
+             mask=_FakeDeviceTensor(torch.uint8, p.total_mask),
+             mask_indptr=_FakeDeviceTensor(torch.int32, p.batch + 1),
+             out=_FakeDeviceTensor(torch.bfloat16, rows * 512),
+             lse=_FakeDeviceTensor(torch.float32, rows))
+    a.update(over)
+    return a
+
+
+def test_binding_checks_tensor_arguments_before_the_call():
+    """Wrong dtype, non-contiguous, host-resident or undersized tensors are
+    refused by the binding before any pointer reaches the C ABI."""
+    import torch
+    p = prob()
+    rows = 9 * 8
+    bad = [dict(q=_FakeDeviceTensor(torch.float32, rows * 576)),
+           dict(q=_FakeDeviceTensor(torch.bfloat16, rows * 576 - 1)),
+           dict(kv_buf=_FakeDeviceTensor(torch.bfloat16, 4096 * 576, contiguous=False)),
+           dict(kv_buf=_FakeDeviceTensor(torch.bfloat16, 4096 * 576, cuda=False)),
+           dict(kv_indices=_FakeDeviceTensor(torch.int64, 30)),
+           dict(kv_indices=_FakeDeviceTensor(torch.int32, 29)),
+           dict(mask=_FakeDeviceTensor(torch.uint8, 269)),
+           dict(mask_indptr=_FakeDeviceTensor(torch.int32, 1)),
+           dict(out=_FakeDeviceTensor(torch.float32, rows * 512)),   # bf16 problem
+           dict(out=_FakeDeviceTensor(torch.bfloat16, rows * 512 - 8)),
+           dict(lse=_FakeDeviceTensor(torch.bfloat16, rows))]
+    for over in bad:
+        a = _args(p, **over)
+        with pytest.raises(ValueError):
+            tv.verify_attn(p, a["q"], a["kv_buf"], a["kv_indices"], a["kv_indptr"],
+                           a["qo_indptr"], a["mask"], a["mask_indptr"], 0.07, a["out"], a["lse"],
+                           None, 0, stream=0)
+    # an fp32-output problem wants 4-byte out elements
+    pf = prob(out_dtype=tv.OUT_F32)
+    a = _args(pf, out=_FakeDeviceTensor(torch.bfloat16, rows * 512))
+    with pytest.raises(ValueError):
+        tv.verify_attn(pf, a["q"], a["kv_buf"], a["kv_indices"], a["kv_indptr"], a["qo_indptr"],
+                       a["mask"], a["mask_indptr"], 0.07, a["out"], a["lse"], None, 0, stream=0)

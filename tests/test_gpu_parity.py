@@ -10,8 +10,10 @@ The probabilities enter the P.V product as bf16.  Rounded once (the default),
 they move an output by at most 2^-8 * max|v_d| (gpu_util.p_rounding_bound):
 with N(0,1) values that stays under the bar, with the x30 outliers of the
 large-batch config it does not, and that config is held to the bar with the
-precise-probability flag (hi + lo pair, bound 2^-16 * max|v_d|) and to the
-derived bound without it.  Visibility handling is checked exactly (same
+precise-probability flag (hi + lo pair, bound 2^-16 * max|v_d|); its
+default-mode run is checked only against that derived bound, which is not the
+bar.  C3, C4 (every row) and S1 also run with fp32 output at the literal bar,
+with no allowance.  Visibility handling is checked exactly (same
 visible-key set per row) and results are checked to be independent of the
 split count: lse within 1e-5 in either mode, outputs within twice the
 rounding bound.
@@ -64,36 +66,77 @@ def test_c2_segmented_batch(out_f32):
     full_check(W.config(2), out_f32=out_f32, label="C2")
 
 
+_ORACLE = {}
+
+
+def oracle_full(name, w):
+    """The oracle over every row of a named configuration, computed once per
+    session (C4's 512 rows x 200k keys take several seconds)."""
+    if name not in _ORACLE:
+        _ORACLE[name] = oracle.run(w)
+    return _ORACLE[name]
+
+
 @pytest.mark.parametrize("num_splits", [0, 32])
 def test_c3_32k_prefix(num_splits):
     print("C3 num_splits=%d" % num_splits, flush=True)
     sampled_check(W.config(3), 96, num_splits=num_splits, label="C3")
 
 
-def test_c4_200k_prefix():
-    print("C4", flush=True)
-    sampled_check(W.config(4), 48, label="C4")
+@pytest.mark.parametrize("num_splits", [0, 32])
+def test_c3_fp32_output_at_the_literal_bar(num_splits):
+    """fp32 output, every row, no allowance: max |diff| <= 8e-3, mean relative
+    error <= 2e-3."""
+    print("C3 fp32 literal bar num_splits=%d" % num_splits, flush=True)
+    w = W.config(3)
+    ro, rl = oracle_full("C3", w)
+    o, l = run(w, num_splits=num_splits, out_f32=True)
+    st = compare(o, l, ro, rl, bf16_out=False, label="C3 f32")
+    print("   %s" % st, flush=True)
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_c4_200k_prefix_every_row(out_f32):
+    """All 512 rows; the fp32 output at the literal bar."""
+    print("C4 every row out_f32=%s" % out_f32, flush=True)
+    w = W.config(4)
+    ro, rl = oracle_full("C4", w)
+    o, l = run(w, out_f32=out_f32)
+    st = compare(o, l, ro, rl, bf16_out=not out_f32, label="C4")
+    print("   %s" % st, flush=True)
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_c5_large_batch_with_outliers(out_f32):
-    """The x30 outliers: the bar with the precise-probability flag."""
+    """The x30 outliers, at the bar, with the precise-probability flag."""
     print("C5 precise out_f32=%s" % out_f32, flush=True)
-    sampled_check(W.config(5), 96, out_f32=out_f32, label="C5 precise", flags=PRECISE)
+    st = sampled_check(W.config(5), 768, out_f32=out_f32, label="C5 precise", flags=PRECISE)
+    print("   %s" % st, flush=True)
 
 
 @pytest.mark.parametrize("out_f32", [False, True])
-def test_c5_default_mode_within_rounding_bound(out_f32):
-    """Without the flag: the bar widened by the derived probability-rounding bound."""
+def test_c5_default_mode_stays_within_its_derived_error_bound(out_f32):
+    """NOT a parity-bar test: without the precise flag the x30 outliers put the
+    probability rounding's derived bound, (2^-8 + 2^-11) * max|v_d| (0.4-0.7
+    absolute per dim at C5), far above the 8e-3 bar, and this mode is checked
+    only against that bound.  C5 meets the bar in precise mode (the test above)."""
     print("C5 default out_f32=%s" % out_f32, flush=True)
     w = W.config(5)
-    sampled_check(w, 96, out_f32=out_f32, label="C5 default",
-                  extra_abs=p_rounding_bound(w, precise=False))
+    st = sampled_check(w, 96, out_f32=out_f32, label="C5 default",
+                       extra_abs=p_rounding_bound(w, precise=False))
+    print("   %s" % st, flush=True)
 
 
-def test_long_prefix_live_shape():
-    print("S1 (32k prefix, n=9, H=8)", flush=True)
-    sampled_check(W.sweep(1), 72, label="S1")
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_long_prefix_live_shape(out_f32):
+    """S1 (the live 9-draft, 8-head shape at a 32k prefix), every row; fp32
+    output at the literal bar."""
+    print("S1 (32k prefix, n=9, H=8) out_f32=%s" % out_f32, flush=True)
+    w = W.sweep(1)
+    ro, rl = oracle_full("S1", w)
+    o, l = run(w, out_f32=out_f32)
+    st = compare(o, l, ro, rl, bf16_out=not out_f32, label="S1")
+    print("   %s" % st, flush=True)
 
 
 # ------------------------------------------------ small shapes, every path
@@ -463,6 +506,40 @@ def test_rows_outside_requests_are_untouched(ns):
         assert np.all(np.isnan(l[:3])) and np.all(np.isnan(l[inside.stop:]))
         ro, rl = oracle.run(w)
         compare(o[inside], l[inside], ro, rl, bf16_out=not out_f32, label="guard ns=%d" % ns)
+
+
+@pytest.mark.parametrize("H", [8, 3])  # mask bytes read in the loop / packed words
+def test_request_longer_than_the_plan_stays_inside_its_buffers(H):
+    """A request of 310 keys under a problem that announces at most 100
+    (max_kv_len, a broken precondition) and one split: the kernels take the
+    plan's ceil(100 / 32) = 4 tiles, the first 128 keys, so nothing is written
+    through the absent partial buffers and no visibility word lands outside
+    its row.  The rows of the request equal the oracle on those 128 keys (mask
+    rows still at their real stride 310); the rows around it keep their
+    canaries."""
+    print("over-long request H=%d" % H, flush=True)
+    import dataclasses
+    w = W.small(604, [300], [10], num_heads=H)
+    L, n = int(w.kv_lens[0]), int(w.q_lens[0])
+    assert L == 310
+    rng = np.random.default_rng(604)
+    front = W.bf16_round(rng.standard_normal((2, H, 576), dtype=np.float32))
+    back = W.bf16_round(rng.standard_normal((3, H, 576), dtype=np.float32))
+    wg = dataclasses.replace(w, q=np.concatenate([front, w.q, back]),
+                             qo_indptr=(w.qo_indptr + 2).astype(np.int32))
+    g = GpuCall(wg, num_splits=1, out_f32=True, max_kv_len=100)
+    assert g.plan["max_splits"] == 1 and g.plan["merge"] == 0
+    g.call()
+    o, l = g.result()
+    inside = slice(2, 2 + n)
+    assert np.all(np.isnan(o[:2])) and np.all(np.isnan(o[inside.stop:]))
+    assert np.all(np.isnan(l[:2])) and np.all(np.isnan(l[inside.stop:]))
+    cut = dataclasses.replace(
+        w, kv_indices=w.kv_indices[:128].copy(), kv_indptr=np.array([0, 128], np.int32),
+        mask=w.mask.reshape(n, L)[:, :128].copy().reshape(-1),
+        mask_indptr=np.array([0, n * 128], np.int32))
+    ro, rl = oracle.run(cut)
+    compare(o[inside], l[inside], ro, rl, bf16_out=False, label="over-long H=%d" % H)
 
 
 def test_graph_replay_follows_new_lengths_within_bounds():

@@ -132,13 +132,73 @@ def workspace_bytes(problem: Problem) -> int:
     return int(_lib.tv_workspace_bytes(ctypes.byref(problem)))
 
 
+def _need(name: str, x, elem_bytes, count: int):
+    """A tensor argument must be a contiguous device tensor with elements of
+    `elem_bytes` bytes (an int or a tuple of allowed sizes) and at least `count`
+    of them; raw pointers (ints) and None pass unchecked (the C ABI checks
+    NULL).  Metadata only: the data is never read here."""
+    if x is None or isinstance(x, int):
+        return
+    sizes = elem_bytes if isinstance(elem_bytes, tuple) else (elem_bytes,)
+    if not x.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if x.element_size() not in sizes:
+        raise ValueError("%s has %d-byte elements, expected %s" % (name, x.element_size(), sizes))
+    if x.numel() < count:
+        raise ValueError("%s holds %d elements, the problem needs %d" % (name, x.numel(), count))
+
+
+def _check_verify_args(p: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask,
+                       mask_indptr, out, lse):
+    """The extents tv_verify_attn reads and writes, from the problem's host-side
+    bounds (q / out / lse rows, pool rows, index and mask entries)."""
+    import torch
+    rows = int(p.total_q) * int(p.num_heads)
+    _need("q", q, 2, rows * QK_DIM)
+    _need("kv_buf", kv_buf, 2, int(p.num_slots) * QK_DIM)
+    _need("kv_indices", kv_indices, 4, int(p.total_kv))
+    for name, x in (("kv_indptr", kv_indptr), ("qo_indptr", qo_indptr),
+                    ("mask_indptr", mask_indptr)):
+        _need(name, x, 4, int(p.batch) + 1)
+    _need("mask", mask, 1, int(p.total_mask))
+    _need("out", out, 4 if p.out_dtype == OUT_F32 else 2, rows * V_DIM)
+    _need("lse", lse, 4, rows)
+    for name, x, dts in (("q", q, (torch.bfloat16, torch.int16, torch.uint16)),
+                         ("kv_buf", kv_buf, (torch.bfloat16, torch.int16, torch.uint16)),
+                         ("out", out, (torch.float32,) if p.out_dtype == OUT_F32 else
+                          (torch.bfloat16, torch.int16, torch.uint16)),
+                         ("lse", lse, (torch.float32,)),
+                         ("kv_indices", kv_indices, (torch.int32,)),
+                         ("kv_indptr", kv_indptr, (torch.int32,)),
+                         ("qo_indptr", qo_indptr, (torch.int32,)),
+                         ("mask_indptr", mask_indptr, (torch.int32,)),
+                         ("mask", mask, (torch.uint8, torch.int8, torch.bool))):
+        if x is not None and not isinstance(x, int) and x.dtype not in dts:
+            raise ValueError("%s has dtype %s, expected one of %s" % (name, x.dtype, dts))
+
+
+def _ws_bytes(workspace, workspace_nbytes):
+    if workspace_nbytes is None:
+        return 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    if workspace is not None and not isinstance(workspace, int):
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        if workspace.numel() * workspace.element_size() < int(workspace_nbytes):
+            raise ValueError("workspace is smaller than the workspace_nbytes passed")
+    return int(workspace_nbytes)
+
+
 def verify_attn(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr,
                 sm_scale: float, out, lse, workspace, workspace_nbytes: int = None, stream=None):
     """Enqueue tv_verify_attn on `stream` (default: torch's current stream).
-    Tensors are device tensors (or raw device pointers as ints)."""
-    if workspace_nbytes is None:
-        workspace_nbytes = 0 if workspace is None else (
-            workspace.numel() * workspace.element_size() if not isinstance(workspace, int) else 0)
+    Tensors are device tensors (or raw device pointers as ints); each tensor's
+    dtype, contiguity, device and size are checked against the problem first."""
+    _check_verify_args(problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr,
+                       out, lse)
+    workspace_nbytes = _ws_bytes(workspace, workspace_nbytes)
     rc = _lib.tv_verify_attn(ctypes.byref(problem), _ptr(q), _ptr(kv_buf), _ptr(kv_indices),
                              _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
                              float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -151,6 +211,9 @@ def verify_attn_timed(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_ind
                       mask_indptr, sm_scale: float, out, lse, workspace, workspace_nbytes: int,
                       split_start_event: int, split_stop_event: int, stream=None):
     """tv_verify_attn_timed: events (raw hipEvent_t handles) bracket the split kernel."""
+    _check_verify_args(problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr,
+                       out, lse)
+    workspace_nbytes = _ws_bytes(workspace, workspace_nbytes)
     rc = _lib.tv_verify_attn_timed(ctypes.byref(problem), _ptr(q), _ptr(kv_buf), _ptr(kv_indices),
                                    _ptr(kv_indptr), _ptr(qo_indptr), _ptr(mask), _ptr(mask_indptr),
                                    float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),

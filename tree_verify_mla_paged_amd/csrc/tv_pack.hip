@@ -135,7 +135,10 @@ __global__ __launch_bounds__(256) void tv_pack_mask_kernel(PackParams p) {
     if (lane == 2 * j + 1) mine = (uint32_t)(bal >> 32);
   }
   const int tile = c * 2 * PACK_SEGS + lane;
-  if (lane < 2 * PACK_SEGS && tile < tiles) p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = mine;
+  // (tiles past max_tiles exist only for a request longer than max_kv_len, a
+  // broken precondition: their words are not stored, so the row stays inside)
+  if (lane < 2 * PACK_SEGS && tile < min(tiles, p.max_tiles))
+    p.words[(int64_t)(q0 + i) * p.max_tiles + tile] = mine;
 }
 
 hipError_t launch_pack(const PackParams& p, int grid_x, int batch, hipStream_t st) {

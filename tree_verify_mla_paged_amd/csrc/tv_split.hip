@@ -993,19 +993,25 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   const int q0 = qo_indptr_[b];
   const int nq = qo_indptr_[b + 1] - q0;
   const int k0 = kv_indptr_[b];
-  const int L = kv_indptr_[b + 1] - k0;
+  const int L = kv_indptr_[b + 1] - k0;  // the mask's row stride
   const int H = p.num_heads;
   const int R = nq * H;
   const int row0 = rb * ROWS_PER_WG;
   if (row0 >= R) return;
-  const int nsplit = L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1;
+  // Keys considered: at most the plan's max_tiles * 32, so a request longer
+  // than max_kv_len (a broken precondition) still stays inside the plan: with
+  // split_keys a multiple of 32 that caps the split count at max_splits (the
+  // partial buffers' extent, absent with one split) and the visibility word of
+  // every tile inside its row.
+  const int Lk = min(L, p.max_tiles * TILE);
+  const int nsplit = Lk > 0 ? (Lk + p.split_keys - 1) / p.split_keys : 1;
   if (s >= nsplit) return;
 
   SplitCtx c;
   c.kv = kv_;
   c.idx = kv_indices_ + k0;
   c.kbeg = s * p.split_keys;
-  c.kend = min(L, c.kbeg + p.split_keys);
+  c.kend = min(Lk, c.kbeg + p.split_keys);
   c.ntiles = c.kend > c.kbeg ? (c.kend - c.kbeg + TILE - 1) / TILE : 0;
   c.wave = wave;
   c.lane = lane;
