@@ -52,7 +52,8 @@ typedef enum {
   TV_ERR_UNSUPPORTED = 4, /* out_dtype or a flags bit unknown, reserved != 0             */
   TV_ERR_INPUT = 5,       /* tv_check_inputs found a device-side precondition violated   */
   TV_ERR_LAUNCH = 6,      /* a kernel launch failed (e.g. the current device is not gfx950) */
-  TV_ERR_HIP = 7          /* a HIP runtime call inside tv_check_inputs failed            */
+  TV_ERR_HIP = 7          /* a HIP runtime call inside tv_check_inputs failed, or the
+                             static scratch lookup of tv_verify_attn_static             */
 } tv_status;
 
 typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
@@ -176,6 +177,34 @@ tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* k
                                const int32_t* mask_indptr, float sm_scale, void* out,
                                float* lse, void* workspace, size_t workspace_bytes,
                                void* split_start_event, void* split_stop_event, void* stream);
+
+/* Bytes of the device-resident scratch array behind tv_verify_attn_static. */
+#define TV_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * tv_verify_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The same arguments, plan and kernels as
+ * tv_verify_attn; the workspace is a static device array of
+ * TV_STATIC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds
+ * from the first use until the process ends.  Nothing is allocated.
+ *
+ * Limit: a problem whose tv_workspace_bytes() exceeds TV_STATIC_SCRATCH_BYTES
+ * returns TV_ERR_WORKSPACE before anything is enqueued (for example 32 requests
+ * x 24 drafts x 64 heads split 11 ways needs about 553 MB; one request of 32
+ * drafts x 16 heads over 32k keys needs 32 MB).  The first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress; TV_ERR_HIP if
+ * that fails), so make it outside stream capture; later calls on the device
+ * make no runtime call besides the launches.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (two streams, two threads) race.  A
+ * call writes every scratch byte it reads, so nothing is cleared between
+ * calls.  Errors otherwise as tv_verify_attn.
+ */
+tv_status tv_verify_attn_static(const tv_problem* p, const void* q, const void* kv_buf,
+                                const int32_t* kv_indices, const int32_t* kv_indptr,
+                                const int32_t* qo_indptr, const uint8_t* mask,
+                                const int32_t* mask_indptr, float sm_scale, void* out,
+                                float* lse, void* stream);
 
 /*
  * Debug validator for the device-side preconditions of tv_verify_attn.  Copies

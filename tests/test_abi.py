@@ -322,3 +322,26 @@ def test_binding_checks_tensor_arguments_before_the_call():
     with pytest.raises(ValueError):
         tv.verify_attn(pf, a["q"], a["kv_buf"], a["kv_indices"], a["kv_indptr"], a["qo_indptr"],
                        a["mask"], a["mask_indptr"], 0.07, a["out"], a["lse"], None, 0, stream=0)
+
+
+def test_static_entry_point_rejects_plans_beyond_its_scratch():
+    """tv_verify_attn_static takes its workspace from a fixed device array: a
+    plan needing more returns TV_ERR_WORKSPACE before anything is enqueued (the
+    fake pointers are never touched); one that needs none, or a bad problem,
+    is decided by the same checks as tv_verify_attn."""
+    fake = 1 << 20
+    args = [fake] * 7
+    # 32 requests x 24 drafts x 64 heads over prefixes up to 65k keys: hundreds of MB
+    big = prob(batch=32, num_heads=64, total_q=768, max_q_len=24, max_kv_len=65560,
+               total_kv=377000, total_mask=24 * 377000, num_slots=524288)
+    assert tv.workspace_bytes(big) > tv.STATIC_SCRATCH_BYTES
+    assert tv.verify_attn_static_status(big, *args, 0.07, fake, fake) == 3
+    # 32 drafts x 16 heads over 32800 keys: 32 MB of partials, within the array
+    c3 = prob(num_heads=16, total_q=32, max_q_len=32, max_kv_len=32800, total_kv=32800,
+              total_mask=32 * 32800, num_slots=200000)
+    assert 0 < tv.workspace_bytes(c3) <= tv.STATIC_SCRATCH_BYTES
+    # the problem's own checks come first
+    assert tv.verify_attn_static_status(prob(num_heads=0), *args, 0.07, fake, fake) == 2
+    assert tv.verify_attn_static_status(prob(), *args, float("nan"), fake, fake) == 2
+    p0 = prob(batch=0, total_q=0, max_q_len=0)
+    assert tv.verify_attn_static_status(p0, 0, 0, 0, 0, 0, 0, 0, 0.07, 0, 0) == 0

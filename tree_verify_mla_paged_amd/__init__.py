@@ -24,8 +24,9 @@ STATUS = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_WORKSPACE"
           4: "TV_ERR_UNSUPPORTED", 5: "TV_ERR_INPUT", 6: "TV_ERR_LAUNCH", 7: "TV_ERR_HIP"}
 
 EXPORTS = ("tv_get_plan", "tv_workspace_bytes", "tv_verify_attn", "tv_verify_attn_timed",
-           "tv_check_inputs", "tv_append_draft",
+           "tv_verify_attn_static", "tv_check_inputs", "tv_append_draft",
            "tv_status_str")
+STATIC_SCRATCH_BYTES = 64 << 20  # the static scratch array behind tv_verify_attn_static
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +81,9 @@ _lib.tv_verify_attn.restype = ctypes.c_int
 _lib.tv_verify_attn_timed.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                       _vp, _vp, ctypes.c_size_t, _vp, _vp, _vp]
 _lib.tv_verify_attn_timed.restype = ctypes.c_int
+_lib.tv_verify_attn_static.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                       _vp, _vp]
+_lib.tv_verify_attn_static.restype = ctypes.c_int
 _lib.tv_check_inputs.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_int32)]
 _lib.tv_check_inputs.restype = ctypes.c_int
 _lib.tv_append_draft.argtypes = [ctypes.POINTER(AppendProblem)] + [_vp] * 12
@@ -221,6 +225,31 @@ def verify_attn_timed(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_ind
                                    int(split_stop_event), _stream(stream))
     if rc != 0:
         raise TreeVerifyError(rc, "tv_verify_attn_timed")
+
+
+def verify_attn_static(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask,
+                       mask_indptr, sm_scale: float, out, lse, stream=None):
+    """Enqueue tv_verify_attn_static: no workspace argument, the library's
+    static device scratch (STATIC_SCRATCH_BYTES per GPU) instead.  Calls that
+    overlap on one GPU race."""
+    _check_verify_args(problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr,
+                       out, lse)
+    rc = _lib.tv_verify_attn_static(ctypes.byref(problem), _ptr(q), _ptr(kv_buf),
+                                    _ptr(kv_indices), _ptr(kv_indptr), _ptr(qo_indptr),
+                                    _ptr(mask), _ptr(mask_indptr), float(sm_scale), _ptr(out),
+                                    _ptr(lse), _stream(stream))
+    if rc != 0:
+        raise TreeVerifyError(rc, "tv_verify_attn_static")
+
+
+def verify_attn_static_status(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr,
+                              mask, mask_indptr, sm_scale: float, out, lse,
+                              stream: int = 0) -> int:
+    """tv_verify_attn_static returning the raw status code (argument-checking tests)."""
+    return int(_lib.tv_verify_attn_static(ctypes.byref(problem), _ptr(q), _ptr(kv_buf),
+                                          _ptr(kv_indices), _ptr(kv_indptr), _ptr(qo_indptr),
+                                          _ptr(mask), _ptr(mask_indptr), float(sm_scale),
+                                          _ptr(out), _ptr(lse), int(stream)))
 
 
 def verify_attn_status(problem: Problem, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask,

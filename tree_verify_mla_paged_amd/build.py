@@ -7,7 +7,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SO = os.path.join(PKG, "libtreeverify.so")
 SOURCES = [os.path.join(PKG, "csrc", f) for f in
-           ("tv_split.hip", "tv_merge.hip", "tv_pack.hip", "tv_append.hip", "tv_api.cpp")]
+           ("tv_split.hip", "tv_merge.hip", "tv_pack.hip", "tv_append.hip", "tv_static.hip",
+            "tv_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # packed fp32 VALU ops stay off (see the kernel notes)

@@ -308,6 +308,23 @@ tv_status tv_verify_attn_timed(const tv_problem* p, const void* q, const void* k
                 static_cast<hipEvent_t>(split_stop_event), stream);
 }
 
+tv_status tv_verify_attn_static(const tv_problem* p, const void* q, const void* kv_buf,
+                                const int32_t* kv_indices, const int32_t* kv_indptr,
+                                const int32_t* qo_indptr, const uint8_t* mask,
+                                const int32_t* mask_indptr, float sm_scale, void* out,
+                                float* lse, void* stream) {
+  Layout lay;
+  const tv_status st = make_layout(p, &lay);
+  if (st != TV_OK) return st;
+  if (lay.plan.workspace_bytes > (int64_t)TV_STATIC_SCRATCH_BYTES) return TV_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (lay.active && lay.plan.workspace_bytes > 0 && tv::static_scratch(&scratch) != hipSuccess)
+    return TV_ERR_HIP;
+  return verify(p, q, kv_buf, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, out,
+                lse, scratch, scratch ? (size_t)TV_STATIC_SCRATCH_BYTES : 0, nullptr, nullptr,
+                stream);
+}
+
 tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
                           const int32_t* kv_indptr, const int32_t* qo_indptr,
                           const int32_t* mask_indptr, void* stream, int32_t* bad_request) {

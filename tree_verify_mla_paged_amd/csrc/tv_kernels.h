@@ -129,5 +129,8 @@ hipError_t launch_merge(const MergeParams& p, int rows, int batch, int out, bool
 constexpr int merge_wave_splits(bool f16_parts) { return f16_parts ? 32 : 16; }
 hipError_t launch_merge_rows(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
                              hipStream_t st);
+// The current device's copy of the static scratch array (tv_static.hip):
+// TV_STATIC_SCRATCH_BYTES bytes, 256-byte aligned.
+hipError_t static_scratch(void** ptr);
 
 }  // namespace tv
