@@ -19,7 +19,7 @@ _lib = None
 ERRORS = {0: "ok", -1: "null pointer", -2: "bad shape", -3: "bad indptr",
           -4: "kv length shorter than draft count (draft slots missing from kv_indices)",
           -5: "mask block is not n_b * L_b bytes (n_b * n_b prefix-visible): wrong mask stride",
-          -6: "slot index outside the pool", -7: "allocation failed"}
+          -6: "slot outside the pool", -7: "allocation failed"}
 
 
 class OracleError(ValueError):
@@ -35,7 +35,8 @@ class _Args(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("num_slots", ctypes.c_int64),
                 ("total_kv", ctypes.c_int64), ("total_mask", ctypes.c_int64),
-                ("sm_scale", ctypes.c_float), ("prefix_visible", ctypes.c_int32)]
+                ("sm_scale", ctypes.c_float), ("prefix_visible", ctypes.c_int32),
+                ("contiguous_prefix", ctypes.c_int32)]
 
 
 def _load():
@@ -60,7 +61,7 @@ def _c(a, dtype):
 
 
 def _pack(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, num_heads,
-          prefix_visible=False):
+          prefix_visible=False, contiguous_prefix=False):
     keep = [_c(q, np.uint16), _c(kv, np.uint16), _c(kv_indices, np.int32), _c(kv_indptr, np.int32),
             _c(qo_indptr, np.int32), _c(mask, np.uint8), _c(mask_indptr, np.int32)]
     q_, kv_, ki, kp, qp, m, mp = keep
@@ -70,25 +71,28 @@ def _pack(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, 
         raise ValueError("kv must be [num_slots, 576] bf16 bits")
     a = _Args(q_.ctypes.data, kv_.ctypes.data, ki.ctypes.data, kp.ctypes.data, qp.ctypes.data,
               m.ctypes.data, mp.ctypes.data, len(qp) - 1, num_heads, q_.shape[0], kv_.shape[0],
-              ki.size, m.size, float(np.float32(sm_scale)), int(bool(prefix_visible)))
+              ki.size, m.size, float(np.float32(sm_scale)), int(bool(prefix_visible)),
+              int(bool(contiguous_prefix)))
     return a, keep
 
 
 def check(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, num_heads,
-          prefix_visible=False) -> int:
+          prefix_visible=False, contiguous_prefix=False) -> int:
     a, keep = _pack(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, num_heads,
-                    prefix_visible)
+                    prefix_visible, contiguous_prefix)
     return _load().tvo_check(ctypes.byref(a))
 
 
 def attention(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, num_heads,
-              rows: Optional[Sequence[int]] = None, threads: int = 0, prefix_visible=False):
+              rows: Optional[Sequence[int]] = None, threads: int = 0, prefix_visible=False,
+              contiguous_prefix=False):
     """fp64 outputs.  rows=None -> (out [N, H, 512], lse [N, H]); otherwise row ids
     g = token * H + head -> (out [len(rows), 512], lse [len(rows)]).
     prefix_visible: the mask holds the draft keys only (n_b x n_b per request)
-    and every prefix key is visible."""
+    and every prefix key is visible.  contiguous_prefix: the prefix keys of
+    request b are the pool run starting at kv_indices[kv_indptr[b]]."""
     a, keep = _pack(q, kv, kv_indices, kv_indptr, qo_indptr, mask, mask_indptr, sm_scale, num_heads,
-                    prefix_visible)
+                    prefix_visible, contiguous_prefix)
     N = keep[0].shape[0]
     if rows is None:
         nrows, rp = N * num_heads, None
@@ -111,12 +115,14 @@ def run(w, rows=None, threads: int = 0):
     """Oracle on a tv_workload.Workload."""
     return attention(w.q, w.kv, w.kv_indices, w.kv_indptr, w.qo_indptr, w.mask, w.mask_indptr,
                      w.sm_scale, w.num_heads, rows=rows, threads=threads,
-                     prefix_visible=getattr(w, "prefix_visible", False))
+                     prefix_visible=getattr(w, "prefix_visible", False),
+                     contiguous_prefix=getattr(w, "contiguous_prefix", False))
 
 
 def check_workload(w) -> int:
     return check(w.q, w.kv, w.kv_indices, w.kv_indptr, w.qo_indptr, w.mask, w.mask_indptr,
-                 w.sm_scale, w.num_heads, prefix_visible=getattr(w, "prefix_visible", False))
+                 w.sm_scale, w.num_heads, prefix_visible=getattr(w, "prefix_visible", False),
+                 contiguous_prefix=getattr(w, "contiguous_prefix", False))
 
 
 def max_threads() -> int:

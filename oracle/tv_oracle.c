@@ -23,6 +23,12 @@
  *    P_b = L_b - n_b prefix keys, and the block of request b holds only the
  *    draft keys, n_b x n_b bytes with row stride n_b: byte i * n_b + k says
  *    whether row i sees key P_b + k.
+ *  - Contiguous-prefix form (the pages' defragmented cache, where a request's
+ *    KV sits in one run of the pool: page 2, section "The Broader Context";
+ *    page 3, section "Conclusion"): the P_b prefix keys of request b are the
+ *    consecutive pool rows kv_indices[kv_indptr[b]] + j, j < P_b, and only
+ *    that first prefix entry of kv_indices is read; the draft keys are looked
+ *    up as before.
  *  - Absorbed MLA: a query row and a key row have 576 dims (512 latent + 64
  *    RoPE, page 3, section "Input Knowledge Required"); the score uses all
  *    576, the value is the first 512 dims of the same key row.
@@ -72,10 +78,25 @@ int tvo_check(const tvo_args* a) {
     /* draft slots are part of kv_indices, so every draft row has its own key */
     if (L < n) return TVO_ERR_KVLEN;
     if (m1 - m0 != n * (a->prefix_visible ? n : L)) return TVO_ERR_MASKLEN;
-    for (int64_t j = k0; j < k1; ++j)
+    /* keys whose slot is read from kv_indices; with a contiguous prefix the
+       run [start, start + P_b) must lie in the pool */
+    int64_t first = k0;
+    if (a->contiguous_prefix && L > n) {
+      const int64_t start = a->kv_indices[k0];
+      if (start < 0 || start + (L - n) > a->num_slots) return TVO_ERR_SLOT;
+      first = k0 + (L - n);
+    }
+    for (int64_t j = first; j < k1; ++j)
       if (a->kv_indices[j] < 0 || a->kv_indices[j] >= a->num_slots) return TVO_ERR_SLOT;
   }
   return TVO_OK;
+}
+
+/* Pool slot of key j of the request whose keys start at kv_indices[k0]; P keys
+ * of prefix (used with a contiguous prefix only). */
+static int64_t key_slot(const tvo_args* a, int64_t k0, int64_t P, int64_t j) {
+  if (a->contiguous_prefix && j < P) return (int64_t)a->kv_indices[k0] + j;
+  return a->kv_indices[k0 + j];
 }
 
 /* request that owns query token t, or -1 */
@@ -102,6 +123,7 @@ static void one_row(const tvo_args* a, int64_t t, int32_t h, double* o, double* 
   const int64_t L = a->kv_indptr[b + 1] - k0;
   const int64_t n = a->qo_indptr[b + 1] - a->qo_indptr[b];
   const int64_t P = a->prefix_visible ? L - n : 0; /* keys visible without a mask byte */
+  const int64_t Pk = L - n;                         /* prefix keys */
   const uint8_t* mrow = a->mask + a->mask_indptr[b] + i * (a->prefix_visible ? n : L);
   const uint16_t* qrow = a->q + ((size_t)t * a->num_heads + h) * QK;
   const double c = (double)a->sm_scale; /* the fp32 scale, widened exactly */
@@ -118,7 +140,7 @@ static void one_row(const tvo_args* a, int64_t t, int32_t h, double* o, double* 
   /* pass 1: scaled scores over all 576 dims, and their maximum */
   double m = -INFINITY;
   for (int64_t v = 0; v < nv; ++v) {
-    const uint16_t* k = a->kv + (size_t)a->kv_indices[k0 + jbuf[v]] * QK;
+    const uint16_t* k = a->kv + (size_t)key_slot(a, k0, Pk, jbuf[v]) * QK;
     double acc = 0.0;
     for (int d = 0; d < QK; ++d) acc += qd[d] * bf16_to_double(k[d]);
     sbuf[v] = c * acc;
@@ -132,7 +154,7 @@ static void one_row(const tvo_args* a, int64_t t, int32_t h, double* o, double* 
     z += w;
   }
   for (int64_t v = 0; v < nv; ++v) {
-    const uint16_t* k = a->kv + (size_t)a->kv_indices[k0 + jbuf[v]] * QK;
+    const uint16_t* k = a->kv + (size_t)key_slot(a, k0, Pk, jbuf[v]) * QK;
     const double w = sbuf[v];
     for (int d = 0; d < VD; ++d) o[d] += w * bf16_to_double(k[d]);
   }

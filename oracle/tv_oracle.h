@@ -15,7 +15,7 @@ enum {
   TVO_ERR_KVLEN = -4,    /* L_b < n_b: draft slots missing from kv_indices      */
   TVO_ERR_MASKLEN = -5,  /* mask block of request b is not n_b * L_b bytes
                             (n_b * n_b in the prefix-visible form)               */
-  TVO_ERR_SLOT = -6,     /* a kv_indices entry is outside [0, num_slots)         */
+  TVO_ERR_SLOT = -6,     /* a key's slot is outside [0, num_slots)               */
   TVO_ERR_ALLOC = -7
 };
 
@@ -37,6 +37,12 @@ typedef struct {
   int32_t prefix_visible;      /* 0: block b is n_b x L_b bytes, stride L_b.
                                   1: block b is n_b x n_b bytes (the draft keys,
                                   stride n_b) and every prefix key is visible  */
+  int32_t contiguous_prefix;   /* 0: key j of request b is slot
+                                  kv_indices[kv_indptr[b] + j].
+                                  1: for j < P_b = L_b - n_b it is slot
+                                  kv_indices[kv_indptr[b]] + j (the prefix is one
+                                  run of the pool); the other prefix entries
+                                  are not read                                  */
 } tvo_args;
 
 /* Validate every precondition; TVO_OK or the first violation found. */

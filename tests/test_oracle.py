@@ -496,6 +496,90 @@ def test_prefix_visible_form_needs_a_visible_prefix():
         W.prefix_visible_form(w)
 
 
+# ------------------------------------------ contiguous-prefix form (N4)
+
+CONTIG = [(41, [100], [5], 4), (42, [300, 7, 0, 95], [3, 2, 0, 6], 3), (43, [0], [4], 2),
+          (44, [33, 1], [1, 7], 5)]
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H", CONTIG)
+def test_contiguous_prefix_form_equals_the_full_key_list(seed, prefix, ndraft, H):
+    """With each prefix one run of the pool, the form that keeps only the run's
+    first slot (the other prefix entries -1) selects the same keys in the same
+    order as the full key list: bit-identical."""
+    w = W.small(seed, prefix, ndraft, num_heads=H, placement="contiguous")
+    c = W.contiguous_prefix_form(w)
+    assert (c.kv_indices == -1).sum() == sum(max(p - 1, 0) for p in prefix)
+    a, la = oracle.run(w)
+    b, lb = oracle.run(c)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # read as a full key list, the -1 entries are slots outside the pool
+    assert oracle.check(c.q, c.kv, c.kv_indices, c.kv_indptr, c.qo_indptr, c.mask, c.mask_indptr,
+                        c.sm_scale, c.num_heads) == (-6 if max(prefix) > 1 else 0)
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H", CONTIG)
+def test_placement_does_not_change_the_result(seed, prefix, ndraft, H):
+    """The generator draws the same key values, in key order, under both
+    placements: random single slots and contiguous runs (in the contiguous-
+    prefix form) give bit-identical outputs."""
+    r = W.small(seed, prefix, ndraft, num_heads=H)
+    c = W.contiguous_prefix_form(W.small(seed, prefix, ndraft, num_heads=H,
+                                         placement="contiguous"))
+    assert not np.array_equal(r.kv_indices[:3], c.kv_indices[:3])
+    a, la = oracle.run(r)
+    b, lb = oracle.run(c)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_contiguous_prefix_closed_form():
+    """q = 0: every visible key weighs the same, so the output is the mean of
+    the visible value rows, listed here by hand.  Pool of 8 rows with distinct
+    values; the prefix run starts at slot 2 (keys at slots 2, 3, 4), the two
+    drafts sit at slots 7 and 0; the middle prefix entries hold slots 5 and 6,
+    which a reader of the full list would gather instead."""
+    H = 2
+    kv = np.zeros((8, 576), np.float32)
+    for s_ in range(8):
+        kv[s_, :512] = np.arange(512) * 0.001 + s_
+        kv[s_, 512:] = -s_
+    w = W.Workload(q=W.bf16_round(np.zeros((2, H, 576), np.float32)), kv=W.bf16_round(kv),
+                   kv_indices=np.array([2, 5, 6, 7, 0], np.int32),
+                   kv_indptr=np.array([0, 5], np.int32), qo_indptr=np.array([0, 2], np.int32),
+                   mask=np.array([1, 1, 1, 1, 0, 1, 1, 1, 1, 1], np.uint8),
+                   mask_indptr=np.array([0, 10], np.int32), sm_scale=W.SM_SCALE, num_heads=H,
+                   contiguous_prefix=True)
+    o, l = oracle.run(w)
+    V = f64(w.kv)[:, :512]
+    want0 = (V[2] + V[3] + V[4] + V[7]) / 4          # draft 0 sees its own key (slot 7)
+    want1 = (V[2] + V[3] + V[4] + V[7] + V[0]) / 5   # draft 1 sees both drafts
+    for h in range(H):
+        np.testing.assert_allclose(o[0, h], want0, rtol=1e-15, atol=1e-15)
+        np.testing.assert_allclose(o[1, h], want1, rtol=1e-15, atol=1e-15)
+        assert l[0, h] == pytest.approx(math.log(4), abs=1e-15)
+        assert l[1, h] == pytest.approx(math.log(5), abs=1e-15)
+    # the full-list reading of the same arrays gathers slots 5 and 6
+    o2, _ = oracle.attention(w.q, w.kv, w.kv_indices, w.kv_indptr, w.qo_indptr, w.mask,
+                             w.mask_indptr, w.sm_scale, H)
+    np.testing.assert_allclose(o2[0, 0], (V[2] + V[5] + V[6] + V[7]) / 4, rtol=1e-15)
+
+
+def test_contiguous_prefix_run_must_lie_in_the_pool():
+    w = W.contiguous_prefix_form(W.small(45, [20], [3], num_heads=1, placement="contiguous"))
+    args = lambda ki: (w.q, w.kv, ki, w.kv_indptr, w.qo_indptr, w.mask, w.mask_indptr,  # noqa
+                       w.sm_scale, 1)
+    assert oracle.check(*args(w.kv_indices), contiguous_prefix=True) == 0
+    for start in (-1, w.num_slots - 19, w.num_slots):
+        ki = w.kv_indices.copy()
+        ki[0] = start
+        assert oracle.check(*args(ki), contiguous_prefix=True) == -6, start
+    ki = w.kv_indices.copy()
+    ki[0] = w.num_slots - 20  # the run ends at the pool's last row
+    assert oracle.check(*args(ki), contiguous_prefix=True) == 0
+    ki[21] = w.num_slots      # a draft slot outside the pool
+    assert oracle.check(*args(ki), contiguous_prefix=True) == -6
+
+
 # ------------------------------------------------ the marshaling step
 
 import oracle.marshal as M  # noqa: E402

@@ -130,6 +130,10 @@ class Workload:
     # mask in the prefix-visible form: n_b x n_b bytes per request (draft keys
     # only), every prefix key visible
     prefix_visible: bool = False
+    # contiguous-prefix form: the P_b prefix keys of request b are the pool run
+    # starting at kv_indices[kv_indptr[b]]; the other prefix entries are not
+    # part of the input (filled with -1 here)
+    contiguous_prefix: bool = False
 
     @property
     def batch(self) -> int:
@@ -186,15 +190,51 @@ def _values(rng: np.random.Generator, shape, out_rng: Optional[np.random.Generat
     return bf16_round(x)
 
 
+def contiguous_slots(rng: np.random.Generator, pool: int, prefix_lens: Sequence[int],
+                     n_drafts: Sequence[int]) -> np.ndarray:
+    """Slot list of a batch whose prefixes each sit in one contiguous run of
+    the pool (a defragmented cache): the runs go into the pool in a seeded
+    request order, separated by seeded gaps; the draft tokens take seeded
+    random slots among those left.  Returned in key order: per request its run,
+    then its draft slots."""
+    B = len(prefix_lens)
+    P = np.array(prefix_lens, dtype=np.int64)
+    n = np.array(n_drafts, dtype=np.int64)
+    slack = pool - int(P.sum()) - int(n.sum())
+    if slack < 0:
+        raise ValueError("pool too small")
+    order = rng.permutation(B)
+    gap_max = max(1, slack // (2 * (B + 1)))
+    start = np.zeros(B, dtype=np.int64)
+    pos = int(rng.integers(0, gap_max))
+    for b in order:
+        start[b] = pos
+        pos += int(P[b]) + int(rng.integers(0, gap_max))
+    used = np.zeros(pool, dtype=bool)
+    for b in range(B):
+        used[start[b]:start[b] + P[b]] = True
+    free = np.flatnonzero(~used)
+    drafts = free[rng.permutation(free.size)[:int(n.sum())]]
+    out, d = [], 0
+    for b in range(B):
+        out.append(np.arange(start[b], start[b] + P[b], dtype=np.int64))
+        out.append(drafts[d:d + n[b]])
+        d += int(n[b])
+    return np.concatenate(out).astype(np.int32) if B else np.zeros(0, np.int32)
+
+
 def build(seed: int, prefix_lens: Sequence[int], parents: Sequence[np.ndarray], num_heads: int,
           pool: int, outlier_p: float = 0.0, poison: bool = True, name: str = "",
-          sm_scale: np.float32 = SM_SCALE) -> Workload:
+          sm_scale: np.float32 = SM_SCALE, placement: str = "random") -> Workload:
     """Assemble a segmented batch from per-request prefix lengths and draft trees.
 
-    Slots: one seeded permutation of the pool, consumed in order; each request
-    takes its prefix slots, then one slot per draft token (random 1-slot
-    placement, disjoint across requests).  Only referenced rows get values;
-    the rest are bf16 NaN when ``poison`` (a stray gather then shows up), else 0.
+    Slots (placement="random"): one seeded permutation of the pool, consumed in
+    order; each request takes its prefix slots, then one slot per draft token
+    (random 1-slot placement, disjoint across requests).  placement=
+    "contiguous": each prefix is one run of consecutive slots
+    (contiguous_slots).  The values drawn for the keys, in key order, do not
+    depend on the placement.  Only referenced rows get values; the rest are
+    bf16 NaN when ``poison`` (a stray gather then shows up), else 0.
     """
     rngs = _spawn(seed)
     r_slot, r_q, r_kv, r_out = rngs[1], rngs[2], rngs[3], rngs[4]
@@ -204,8 +244,13 @@ def build(seed: int, prefix_lens: Sequence[int], parents: Sequence[np.ndarray], 
     need = int(L.sum())
     while pool < need:
         pool *= 2
-    perm = r_slot.permutation(pool).astype(np.int32)
-    kv_indices = perm[:need].copy()
+    if placement == "random":
+        perm = r_slot.permutation(pool).astype(np.int32)
+        kv_indices = perm[:need].copy()
+    elif placement == "contiguous":
+        kv_indices = contiguous_slots(r_slot, pool, prefix_lens, n)
+    else:
+        raise ValueError("placement %r" % placement)
     kv_indptr = np.zeros(B + 1, dtype=np.int64)
     kv_indptr[1:] = np.cumsum(L)
     qo_indptr = np.zeros(B + 1, dtype=np.int64)
@@ -278,23 +323,42 @@ def config(k: int, poison: bool = True) -> Workload:
 SWEEP_PREFIX = {1: 32768, 2: 131072, 3: 200000}
 
 
-def sweep(k: int, poison: bool = True) -> Workload:
+def sweep(k: int, poison: bool = True, placement: str = "random") -> Workload:
     """The live shape (n_draft=9, H=8) at long prefixes: 32768 / 131072 / 200000."""
     rngs = _spawn(100 + k)
     parents = [gen_tree(rngs[0], 9)]
-    return build(100 + k, [SWEEP_PREFIX[k]], parents, 8, 262144, poison=poison, name="S%d" % k)
+    return build(100 + k, [SWEEP_PREFIX[k]], parents, 8, 262144, poison=poison, name="S%d" % k,
+                 placement=placement)
 
 
 def small(seed: int, prefix_lens: Sequence[int], n_drafts: Sequence[int], num_heads: int,
           pool: Optional[int] = None, outlier_p: float = 0.0, poison: bool = True,
-          max_branch: Optional[int] = None) -> Workload:
+          max_branch: Optional[int] = None, placement: str = "random") -> Workload:
     """Ad-hoc seeded workload (tests): random trees with the given draft counts."""
     rngs = _spawn(seed)
     parents = [gen_tree(rngs[0], int(n), max_branch=max_branch) for n in n_drafts]
     need = int(sum(prefix_lens) + sum(n_drafts))
     pool = pool if pool is not None else max(64, 2 * need)
     return build(seed, prefix_lens, parents, num_heads, pool, outlier_p=outlier_p, poison=poison,
-                 name="small%d" % seed)
+                 name="small%d" % seed, placement=placement)
+
+
+def contiguous_prefix_form(w: Workload) -> Workload:
+    """The same workload in the contiguous-prefix form: every prefix must be
+    one run of consecutive slots (placement="contiguous"); kv_indices keeps its
+    layout, but of each prefix only the first entry (the run's first slot)
+    stays part of the input; the other prefix entries become -1, which a
+    reader that used them would turn into a slot outside the pool."""
+    ki = w.kv_indices.astype(np.int64).copy()
+    for b in range(w.batch):
+        k0 = int(w.kv_indptr[b])
+        P = int(w.kv_lens[b] - w.q_lens[b])
+        run = ki[k0:k0 + P]
+        if P and not np.array_equal(run, run[0] + np.arange(P)):
+            raise ValueError("request %d: prefix slots are not one contiguous run" % b)
+        ki[k0 + 1:k0 + P] = -1
+    return dataclasses.replace(w, kv_indices=ki.astype(np.int32), contiguous_prefix=True,
+                               name=w.name + "/contiguous-prefix")
 
 
 def prefix_visible_form(w: Workload) -> Workload:
@@ -318,7 +382,8 @@ def prefix_visible_form(w: Workload) -> Workload:
 
 
 def chain(seed: int, prefix_lens: Sequence[int], n: int, num_heads: int,
-          pool: Optional[int] = None, poison: bool = True, name: str = "") -> Workload:
+          pool: Optional[int] = None, poison: bool = True, name: str = "",
+          placement: str = "random") -> Workload:
     """Requests whose n draft tokens form one chain (draft i's parent is i - 1):
     a causal mask over the drafts.  n = 1 is plain decode: one query token per
     request seeing its prefix and itself."""
@@ -326,7 +391,7 @@ def chain(seed: int, prefix_lens: Sequence[int], n: int, num_heads: int,
     need = int(sum(prefix_lens)) + n * len(prefix_lens)
     pool = pool if pool is not None else max(64, 2 * need)
     return build(seed, prefix_lens, parents, num_heads, pool, poison=poison,
-                 name=name or "chain%d" % seed)
+                 name=name or "chain%d" % seed, placement=placement)
 
 
 # Workloads of the same kernels beyond tree verification (not part of the five
@@ -338,11 +403,13 @@ EXTRA_DESC = {
 }
 
 
-def extra(key: str, poison: bool = True) -> Workload:
+def extra(key: str, poison: bool = True, placement: str = "random") -> Workload:
     if key == "D":
-        return chain(301, [32768] * 8, 1, 128, pool=524288, poison=poison, name="D")
+        return chain(301, [32768] * 8, 1, 128, pool=524288, poison=poison, name="D",
+                     placement=placement)
     if key == "K":
-        return chain(302, [32768], 16, 16, pool=200000, poison=poison, name="K")
+        return chain(302, [32768], 16, 16, pool=200000, poison=poison, name="K",
+                     placement=placement)
     raise ValueError("unknown workload %r" % key)
 
 
