@@ -78,25 +78,70 @@ class HipEvents:
         self.lib.hipEventDestroy(ctypes.c_void_p(ev))
 
 
-def workload(cfg: str, poison: bool, prefix_visible: bool = False):
-    w, desc, splits = _workload(cfg, poison)
+def workload(cfg: str, poison: bool, prefix_visible: bool = False, placement: str = "random",
+             contiguous_prefix: bool = False):
+    """The workload of a configuration; placement "contiguous" lays each prefix
+    out as one run of the pool, and contiguous_prefix (which needs it) passes
+    the run by its first slot only (TV_FLAG_CONTIGUOUS_PREFIX)."""
+    if contiguous_prefix:
+        placement = "contiguous"
+    w, desc, splits = _workload(cfg, poison, placement)
     if prefix_visible:
         w = W.prefix_visible_form(w)
         desc += "; mask in the prefix-visible form (draft keys only)"
+    if placement == "contiguous":
+        desc += "; each prefix one contiguous run of the pool"
+    if contiguous_prefix:
+        w = W.contiguous_prefix_form(w)
+        desc += ", passed by its first slot (contiguous-prefix form)"
     return w, desc, splits
 
 
-def _workload(cfg: str, poison: bool):
+def _workload(cfg: str, poison: bool, placement: str = "random"):
     if cfg in W.EXTRA_DESC:
-        return W.extra(cfg, poison=poison), W.EXTRA_DESC[cfg], None
+        return W.extra(cfg, poison=poison, placement=placement), W.EXTRA_DESC[cfg], None
     if cfg.startswith("S"):
         k = int(cfg[1:])
-        w = W.sweep(k, poison=poison)
+        w = W.sweep(k, poison=poison, placement=placement)
         desc = "S%d: 1 request, n_draft=9, prefix %d, H=8 (live shape at long prefix)" % (
             k, W.SWEEP_PREFIX[k])
         return w, desc, None
     k = int(cfg)
-    return W.config(k, poison=poison), W.CONFIG_DESC[k], W.CONFIG_SPLITS.get(k)
+    return (W.config(k, poison=poison, placement=placement), W.CONFIG_DESC[k],
+            W.CONFIG_SPLITS.get(k))
+
+
+def flags_for(args):
+    import tree_verify_mla_paged_amd as tv
+    return ((tv.FLAG_PRECISE_P if args.precise else 0) |
+            (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0) |
+            (tv.FLAG_CONTIGUOUS_PREFIX if args.contiguous_prefix else 0))
+
+
+def bench_workload(args, poison=False):
+    return workload(args.config, poison=poison, prefix_visible=args.prefix_visible,
+                    placement=args.placement, contiguous_prefix=args.contiguous_prefix)
+
+
+def key_slots(w):
+    """Every key's pool slot in key order (the contiguous-prefix form expanded)."""
+    if not w.contiguous_prefix:
+        return w.kv_indices
+    out = w.kv_indices.astype(np.int64).copy()
+    for b in range(w.batch):
+        k0 = int(w.kv_indptr[b])
+        P = int(w.kv_lens[b] - w.q_lens[b])
+        out[k0:k0 + P] = out[k0] + np.arange(P)
+    return out.astype(np.int32)
+
+
+def index_entries(w):
+    """kv_indices entries the call reads: every key's, or with the
+    contiguous-prefix form each request's first prefix entry and its drafts'."""
+    if not w.contiguous_prefix:
+        return int(w.kv_lens.sum())
+    P = w.kv_lens - w.q_lens
+    return int(w.q_lens.sum() + (P > 0).sum())
 
 
 def algorithmic(w):
@@ -105,7 +150,7 @@ def algorithmic(w):
     kv_bytes = w.gathered_kv_bytes()
     nq = w.total_q
     total_bytes = (kv_bytes + nq * H * 576 * 2 + nq * H * 512 * 2 + nq * H * 4 +
-                   int(w.kv_lens.sum()) * 4 + int(w.mask.size))
+                   index_entries(w) * 4 + int(w.mask.size))
     flops = 2.0 * (576 + 512) * H * w.visible_pairs()
     return kv_bytes, total_bytes, flops
 
@@ -121,13 +166,12 @@ def source_hash():
 def plan_for(args):
     """The library's launch plan for the benchmark configuration."""
     import tree_verify_mla_paged_amd as tv
-    w, _, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
+    w, _, cfg_splits = bench_workload(args)
     splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
                         tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
-                        (tv.FLAG_PRECISE_P if args.precise else 0) |
-                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
+                        flags_for(args))
     return launch_shape(tv.plan(p))
 
 
@@ -164,7 +208,7 @@ def counter_workload(args):
     for _ in range(3):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    w, _, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
+    w, _, cfg_splits = bench_workload(args)
     splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in dict(
         q=w.q.view(np.int16), kv=w.kv.view(np.int16), kv_indices=w.kv_indices,
@@ -173,8 +217,7 @@ def counter_workload(args):
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
                         tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
-                        (tv.FLAG_PRECISE_P if args.precise else 0) |
-                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
+                        flags_for(args))
     out = torch.empty((w.total_q, w.num_heads, 512),
                       dtype=torch.float32 if args.out_f32 else torch.bfloat16, device="cuda")
     lse = torch.empty((w.total_q, w.num_heads), dtype=torch.float32, device="cuda")
@@ -481,6 +524,12 @@ def main():
     ap.add_argument("--splits", type=int, default=0,
                     help="KV split count (0 = the library's plan; -1 = the configuration's own "
                          "split count if it names one)")
+    ap.add_argument("--placement", choices=("random", "contiguous"), default="random",
+                    help="pool placement of the keys: random single slots (the configurations') "
+                         "or each prefix one contiguous run")
+    ap.add_argument("--contiguous-prefix", action="store_true",
+                    help="contiguous placement, passed in the contiguous-prefix form (each prefix "
+                         "by its first slot only)")
     ap.add_argument("--out-f32", action="store_true")
     ap.add_argument("--precise", action="store_true",
                     help="probabilities as a bf16 hi + lo pair in the P.V product")
@@ -511,7 +560,7 @@ def main():
     import torch
     import tree_verify_mla_paged_amd as tv
 
-    w, desc, cfg_splits = workload(args.config, poison=False, prefix_visible=args.prefix_visible)
+    w, desc, cfg_splits = bench_workload(args)
     splits = args.splits if args.splits >= 0 else (cfg_splits or 0)
     dev = "cuda"
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in dict(
@@ -521,8 +570,7 @@ def main():
     p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
                         int(w.kv_indices.size), int(w.mask.size), splits,
                         tv.OUT_F32 if args.out_f32 else tv.OUT_BF16,
-                        (tv.FLAG_PRECISE_P if args.precise else 0) |
-                        (tv.FLAG_PREFIX_VISIBLE if args.prefix_visible else 0))
+                        flags_for(args))
     plan = tv.plan(p)
     N, H = w.total_q, w.num_heads
     out = torch.empty((N, H, 512), dtype=torch.float32 if args.out_f32 else torch.bfloat16,
@@ -592,7 +640,8 @@ def main():
     append = append_times(w, args.steps, args.prefix_visible) if args.append else None
     calib = calibration() if not (args.no_calibration or args.timed_only) else None
     if calib:
-        calib["index_select_gather"] = gather_calibration(t["kv"], t["kv_indices"])
+        calib["index_select_gather"] = gather_calibration(
+            t["kv"], torch.from_numpy(key_slots(w)).to(dev))
 
     kv_bytes, total_bytes, flops = algorithmic(w)
     us_per_call = ms_per_step * 1e3
@@ -607,8 +656,9 @@ def main():
         achieved = total_bytes / (split_avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
-    # the counter summary covers the full mask form only
-    roof["traffic"] = (None if args.prefix_visible else
+    # the counter summary covers the full mask form and random placement only
+    roof["traffic"] = (None if (args.prefix_visible or args.placement != "random" or
+                                args.contiguous_prefix) else
                        measured_traffic(args.config, splits, bool(args.precise),
                                         launch_shape(plan)))
     roof["kernel"] = "tv_split_kernel"
@@ -654,6 +704,8 @@ def main():
                    "max_kv_len": int(w.max_kv_len), "heads": H, "num_splits_arg": splits,
                    "plan": plan, "out_dtype": "f32" if args.out_f32 else "bf16",
                    "precise_p": bool(args.precise), "prefix_visible": bool(args.prefix_visible),
+                   "placement": "contiguous" if args.contiguous_prefix else args.placement,
+                   "contiguous_prefix": bool(args.contiguous_prefix),
                    "gathered_kv_bytes": kv_bytes, "visible_pairs_x_heads": w.visible_pairs() * H},
         "roofline": roof,
     }

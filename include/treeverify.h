@@ -79,6 +79,21 @@ typedef enum { TV_OUT_BF16 = 0, TV_OUT_F32 = 1 } tv_out_dtype;
  * The results equal those of the full mask with every prefix byte nonzero. */
 #define TV_FLAG_PREFIX_VISIBLE 2
 
+/* tv_problem.flags.  Each request's prefix keys are one contiguous run of the
+ * pool, as a defragmented cache lays them out (page 2 "Flipping the Switch",
+ * section "The Broader Context", and page 3 "The Pivot to Live Cutover",
+ * section "Conclusion": the serving stack's KV defragmentation): with P_b =
+ * L_b - n_b, prefix key j < P_b of request b is pool slot
+ * kv_indices[kv_indptr[b]] + j.  Of the prefix entries of kv_indices only that
+ * first one is read (none when P_b = 0); the entries kv_indptr[b] + 1 ..
+ * kv_indptr[b] + P_b - 1 are never read and need not be written.  The n_b
+ * draft keys are read from kv_indices as usual.  kv_indptr, the mask and
+ * every other argument keep their meaning; the results equal those of the
+ * full key list start, start + 1, ..., start + P_b - 1 followed by the draft
+ * slots.  The run [start, start + P_b) must lie in the pool (tv_check_inputs
+ * checks it). */
+#define TV_FLAG_CONTIGUOUS_PREFIX 4
+
 /* Host-side description of one call.  Device-side lengths may vary between
  * calls (or graph replays) as long as they stay within these bounds. */
 typedef struct tv_problem {
@@ -215,7 +230,8 @@ tv_status tv_verify_attn_static(const tv_problem* p, const void* q, const void* 
  * indptrs non-decreasing and within total_q / total_kv / total_mask; every
  * n_b <= max_q_len and L_b <= max_kv_len; L_b >= n_b; the mask block of
  * request b is exactly n_b * L_b bytes (n_b * n_b with TV_FLAG_PREFIX_VISIBLE);
- * every slot in [0, num_slots).  The last
+ * every slot in [0, num_slots) (with TV_FLAG_CONTIGUOUS_PREFIX: each prefix
+ * run inside the pool, and the draft slots).  The last
  * two catch both halves of the marshaling mistake the pages describe (page 2,
  * section "The Long Road to Parity"): draft slots missing from kv_indices, and
  * a mask laid out with the prefix-only row stride.  Mask contents are not read.

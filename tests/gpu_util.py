@@ -61,7 +61,8 @@ def problem_for(w: W.Workload, num_splits: int = 0, out_f32: bool = False, max_q
         max_kv_len=w.max_kv_len if max_kv_len is None else max_kv_len,
         num_slots=w.num_slots, total_kv=int(w.kv_indices.size), total_mask=int(w.mask.size),
         num_splits=num_splits, out_dtype=tv.OUT_F32 if out_f32 else tv.OUT_BF16,
-        flags=flags | (tv.FLAG_PREFIX_VISIBLE if w.prefix_visible else 0))
+        flags=flags | (tv.FLAG_PREFIX_VISIBLE if w.prefix_visible else 0) |
+        (tv.FLAG_CONTIGUOUS_PREFIX if w.contiguous_prefix else 0))
 
 
 class GpuCall:

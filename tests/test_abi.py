@@ -135,7 +135,7 @@ def test_bad_shapes_are_rejected():
         with pytest.raises(tv.TreeVerifyError) as e:
             tv.plan(prob(**kw))
         assert e.value.code == 2
-    for kw in [dict(out_dtype=7), dict(flags=4), dict(flags=-1)]:
+    for kw in [dict(out_dtype=7), dict(flags=8), dict(flags=-1)]:
         with pytest.raises(tv.TreeVerifyError) as e:
             tv.plan(prob(**kw))
         assert e.value.code == 4

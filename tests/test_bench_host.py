@@ -52,3 +52,17 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_contiguous_prefix_workload_and_counts():
+    """--contiguous-prefix: contiguous placement, each prefix passed by its first
+    slot; the expanded key list is the placement's, and the index bytes the
+    call reads are one entry per prefix plus one per draft."""
+    w, desc, _ = bench.workload("S1", poison=False, contiguous_prefix=True)
+    full, _, _ = bench.workload("S1", poison=False, placement="contiguous")
+    assert w.contiguous_prefix and "contiguous" in desc
+    assert np.array_equal(bench.key_slots(w), full.kv_indices)
+    assert bench.index_entries(w) == 1 + 9 and bench.index_entries(full) == 32768 + 9
+    _, tot_c, fl_c = bench.algorithmic(w)
+    _, tot_f, fl_f = bench.algorithmic(full)
+    assert fl_c == fl_f and tot_f - tot_c == 4 * 32767

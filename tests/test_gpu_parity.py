@@ -463,6 +463,108 @@ def test_check_inputs_prefix_visible_stride():
     assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"], mp) == (5, 0)
 
 
+# ------------------------------------ contiguous-prefix form (N4)
+
+CONTIG_SHAPES = [
+    # seed, prefix lengths, draft counts, heads, num_splits
+    (311, [100], [5], 8, 0),              # 4 tiles, ragged tail
+    (312, [250], [20], 16, 2),            # the prefix ends inside a tile
+    (313, [300, 7, 0, 95], [3, 2, 0, 6], 5, 4),  # packed words; empty request; no prefix
+    (314, [1000], [9], 8, 7),
+    (315, [0], [4], 3, 0),                # no prefix at all
+    (316, [31, 32, 33], [1, 1, 1], 64, 0),  # prefix ends at, before, after a tile edge
+]
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H,ns", CONTIG_SHAPES)
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_contiguous_prefix_small(seed, prefix, ndraft, H, ns, out_f32):
+    """Each prefix one run of the pool, passed by its first slot only (the
+    other prefix entries of kv_indices are -1, outside the pool)."""
+    print("contiguous prefix seed=%d H=%d ns=%d f32=%s" % (seed, H, ns, out_f32), flush=True)
+    w = W.contiguous_prefix_form(W.small(seed, prefix, ndraft, num_heads=H,
+                                         placement="contiguous"))
+    full_check(w, num_splits=ns, out_f32=out_f32, label="contig%d" % seed)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_contiguous_prefix_gives_the_random_placement_bits(flags):
+    """The generator gives both placements the same key values in key order:
+    the run form of the contiguous placement and the key list of the random
+    placement give bit-identical outputs (S1, and a batch with packed words)."""
+    for make in (lambda pl: W.sweep(1, placement=pl),
+                 lambda pl: W.small(317, [3000, 17, 0, 900], [5, 3, 2, 7], num_heads=7,
+                                    placement=pl)):
+        r = make("random")
+        c = W.contiguous_prefix_form(make("contiguous"))
+        print("contiguous vs random placement: %s flags=%d" % (r.name, flags), flush=True)
+        a = GpuCall(r, out_f32=True, flags=flags)
+        a.call()
+        b = GpuCall(c, out_f32=True, flags=flags)
+        b.call()
+        assert np.array_equal(a.out_bits(), b.out_bits())
+        assert np.array_equal(a.lse.cpu().numpy().view(np.int32),
+                              b.lse.cpu().numpy().view(np.int32))
+
+
+def test_contiguous_prefix_s1_against_the_oracle():
+    print("S1 contiguous prefix", flush=True)
+    w = W.contiguous_prefix_form(W.sweep(1, placement="contiguous"))
+    ro, rl = oracle.run(w)
+    o, l = run(w, out_f32=True)
+    compare(o, l, ro, rl, bf16_out=False, label="S1 contiguous")
+
+
+def test_check_inputs_contiguous_prefix_run():
+    w = W.contiguous_prefix_form(W.small(318, [40, 25], [3, 2], num_heads=8,
+                                         placement="contiguous"))
+    t = upload(w)
+    p = tv.make_problem(w.batch, 8, w.total_q, w.max_q_len, w.max_kv_len, w.num_slots,
+                        int(w.kv_indices.size), int(w.mask.size), flags=tv.FLAG_CONTIGUOUS_PREFIX)
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                           t["mask_indptr"]) == (0, -1)
+    # read as a full key list, the -1 entries are slots outside the pool
+    p.flags = 0
+    assert tv.check_inputs(p, t["kv_indices"], t["kv_indptr"], t["qo_indptr"],
+                           t["mask_indptr"]) == (5, 0)
+    p.flags = tv.FLAG_CONTIGUOUS_PREFIX
+    bad = t["kv_indices"].clone()
+    bad[int(w.kv_indptr[1])] = w.num_slots - 24  # request 1's run of 25 ends past the pool
+    assert tv.check_inputs(p, bad, t["kv_indptr"], t["qo_indptr"], t["mask_indptr"]) == (5, 1)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_contiguous_prefix_pool_beyond_4gib(flags):
+    """The run form in a pool larger than 4 GiB (64-bit gather addresses): the
+    same keys moved to the top of the big pool give the same bits."""
+    print("contiguous prefix, pool beyond 4 GiB flags=%d" % flags, flush=True)
+    w = W.contiguous_prefix_form(W.small(319, [900, 37, 2500], [7, 3, 12], num_heads=8,
+                                         placement="contiguous"))
+    g = GpuCall(w, num_splits=3, out_f32=True, flags=flags)
+    g.call()
+    narrow = g.out_bits().copy()
+    offset = WIDE_SLOTS - w.num_slots
+    big = torch.full((WIDE_SLOTS, 576), 0x7FC0, dtype=torch.int16, device="cuda")
+    big[offset:].copy_(g.t["kv"])
+    ki = g.t["kv_indices"].long()
+    idx = torch.where(ki >= 0, ki + offset, ki).to(torch.int32)  # the -1 entries stay unread
+    p = tv.make_problem(w.batch, w.num_heads, w.total_q, w.max_q_len, w.max_kv_len, WIDE_SLOTS,
+                        int(w.kv_indices.size), int(w.mask.size), 3, tv.OUT_F32,
+                        flags | tv.FLAG_CONTIGUOUS_PREFIX)
+    out = torch.full_like(g.out, float("nan"))
+    lse = torch.full_like(g.lse, float("nan"))
+    ws = torch.empty(max(tv.workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    tv.verify_attn(p, g.t["q"], big, idx, g.t["kv_indptr"], g.t["qo_indptr"], g.t["mask"],
+                   g.t["mask_indptr"], float(w.sm_scale), out, lse, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int32).cpu().numpy(), narrow)
+    o, l = g.result()
+    ro, rl = oracle.run(w)
+    compare(o, l, ro, rl, bf16_out=False, label="contig wide flags=%d" % flags)
+    del big
+    torch.cuda.empty_cache()
+
+
 # ------------------------------ other workloads of the same kernels
 
 @pytest.mark.parametrize("H", [16, 128])

@@ -19,6 +19,7 @@ OUT_BF16 = 0
 OUT_F32 = 1
 FLAG_PRECISE_P = 1  # probabilities as a bf16 hi + lo pair in the P.V product
 FLAG_PREFIX_VISIBLE = 2  # mask holds the draft keys only (n_b x n_b); prefix keys all visible
+FLAG_CONTIGUOUS_PREFIX = 4  # prefix keys are the pool run from kv_indices[kv_indptr[b]]
 
 STATUS = {0: "TV_OK", 1: "TV_ERR_NULL", 2: "TV_ERR_SHAPE", 3: "TV_ERR_WORKSPACE",
           4: "TV_ERR_UNSUPPORTED", 5: "TV_ERR_INPUT", 6: "TV_ERR_LAUNCH", 7: "TV_ERR_HIP"}

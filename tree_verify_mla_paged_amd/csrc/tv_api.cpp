@@ -77,7 +77,8 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   if (p->total_kv > kMaxInt32 || p->total_mask > kMaxInt32 || p->num_slots > kMaxInt32 + 1LL)
     return TV_ERR_SHAPE;
   if (p->out_dtype != TV_OUT_BF16 && p->out_dtype != TV_OUT_F32) return TV_ERR_UNSUPPORTED;
-  if ((p->flags & ~(TV_FLAG_PRECISE_P | TV_FLAG_PREFIX_VISIBLE)) != 0 || p->reserved != 0)
+  if ((p->flags & ~(TV_FLAG_PRECISE_P | TV_FLAG_PREFIX_VISIBLE | TV_FLAG_CONTIGUOUS_PREFIX)) != 0 ||
+      p->reserved != 0)
     return TV_ERR_UNSUPPORTED;
   if (p->max_q_len > p->total_q) return TV_ERR_SHAPE;
   // the pack and merge grids put the request in their y dimension
@@ -238,6 +239,7 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.s.out_f32 = p->out_dtype == TV_OUT_F32 ? 1 : 0;
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
   sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
+  sp.contig = (p->flags & TV_FLAG_CONTIGUOUS_PREFIX) != 0;
   const int grid = (int)lay.grid;
   if (tv::launch_split(sp, grid, s, ev0, ev1) != hipSuccess) return TV_ERR_LAUNCH;
 
@@ -337,6 +339,7 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
   if (p->total_kv > 0 && !kv_indices) return TV_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool prefix_visible = (p->flags & TV_FLAG_PREFIX_VISIBLE) != 0;
+  const bool contig = (p->flags & TV_FLAG_CONTIGUOUS_PREFIX) != 0;
   const size_t nb = (size_t)p->batch + 1;
   std::vector<int32_t> kvp(nb), qop(nb), mp(nb), idx((size_t)p->total_kv);
   if (hipMemcpyAsync(kvp.data(), kv_indptr, nb * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -360,7 +363,18 @@ tv_status tv_check_inputs(const tv_problem* p, const int32_t* kv_indices,
       if (bad_request) *bad_request = b;
       return TV_ERR_INPUT;
     }
-    for (int64_t j = k0; j < k1; ++j) {
+    // keys whose slot comes from kv_indices; a contiguous prefix is the run
+    // [kv_indices[k0], + P_b), which must lie in the pool
+    int64_t first = k0;
+    const int64_t P = (k1 - k0) - (q1 - q0);
+    if (contig && P > 0) {
+      if (idx[k0] < 0 || idx[k0] + P > p->num_slots) {
+        if (bad_request) *bad_request = b;
+        return TV_ERR_INPUT;
+      }
+      first = k0 + P;
+    }
+    for (int64_t j = first; j < k1; ++j) {
       if (idx[j] < 0 || idx[j] >= p->num_slots) {
         if (bad_request) *bad_request = b;
         return TV_ERR_INPUT;

@@ -82,6 +82,9 @@ struct SplitParams {
   SplitScalars s;
   bool wide;                  // pool larger than 4 GiB: 64-bit gather addresses
   bool precise;               // probabilities as bf16 hi + lo in the P.V product
+  // contiguous-prefix form: prefix key j of request b is pool slot
+  // kv_indices[kv_indptr[b]] + j; the other prefix entries are not read
+  bool contig;
 };
 
 struct MergeParams {

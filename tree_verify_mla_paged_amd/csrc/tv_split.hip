@@ -112,6 +112,9 @@ struct SplitCtx {
   uint32_t rp_voff;         // RoPE gather: this lane's 16-byte RoPE chunk within a pool row
   uint32_t m_main, m_rope, m_mask;  // this wave's gather targets within a stage (bytes)
   int kbeg, kend, ntiles;   // key range [kbeg, kend) of the split, its 32-key tiles
+  // contiguous-prefix form: keys below plen are pool slots run0 + key (no
+  // index read); plen = 0 otherwise
+  int run0, plen;
   int wave, lane;
   // per-lane LDS offsets (relative to a stage)
   int qk_off, pv_off, mw_off;
@@ -215,10 +218,23 @@ __device__ __forceinline__ void fence(T& v) {
 // ahead, before the gathers of an earlier tile, so the vmcnt wait that makes
 // that tile readable also covers it, and the slots are then plain LDS reads: no
 // scalar load is ever pending in the tile loop (a pending one would turn every
-// LDS wait into a full wait).
+// LDS wait into a full wait).  CONTIG: a lane whose key lies in the prefix run
+// stores run0 + key into its ring word instead (an LDS store, in order with the
+// wave's later ring reads); only draft keys are loaded, so a tile inside the
+// prefix issues no load at all.
+template <bool CONTIG>
 __device__ __forceinline__ void slot_dma(const SplitCtx& c, int t) {
   const int k = min(c.kbeg + t * TILE + 8 * c.wave + (fresh(c.lane) & 7), c.kend - 1);
-  dma4_s((uint32_t)k * 4u, c.idx, lds_addr(c.sring) + 256 * (t % SLOT_RING));
+  if constexpr (CONTIG) {
+    if (k < c.plen) {
+      *reinterpret_cast<__attribute__((address_space(3))) int*>(
+          c.sring + 256 * (t % SLOT_RING) + 4 * c.lane) = c.run0 + k;
+    } else {
+      dma4_s((uint32_t)k * 4u, c.idx, lds_addr(c.sring) + 256 * (t % SLOT_RING));
+    }
+  } else {
+    dma4_s((uint32_t)k * 4u, c.idx, lds_addr(c.sring) + 256 * (t % SLOT_RING));
+  }
 }
 
 // The 8 slots of a tile as wave-uniform values, and the slot of key 8*wave +
@@ -737,10 +753,11 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, con
 
 // Start of the split (c.ntiles >= 1), in two parts around the query loads.
 // split_slots: the slot loads of tiles 0..2 (nothing outstanding before them).
+template <bool CONTIG>
 __device__ __forceinline__ void split_slots(const SplitCtx& c) {
-  slot_dma(c, 0);
-  slot_dma(c, 1);
-  slot_dma(c, 2);
+  slot_dma<CONTIG>(c, 0);
+  slot_dma<CONTIG>(c, 1);
+  slot_dma<CONTIG>(c, 2);
 }
 // split_gathers: once the slots have landed (the caller waits), the gathers of
 // tiles 0 and 1 and their mask bytes.
@@ -784,7 +801,7 @@ __device__ __forceinline__ int alpha_moved(float a0, float a1) {
 // holds tile t+1's, turned into the word early in the chain, and then receives
 // tile t+2's); the softmax's first step picks one (MaskSel), so that nothing
 // in the chain waits for the word's LDS read.
-template <bool WIDE, bool PRECISE, bool GATHER>
+template <bool WIDE, bool PRECISE, bool GATHER, bool CONTIG>
 __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
                                            const bf16x8 (&qf)[QK / 16], const float* alpha_t,
                                            int t, int cur, int nx1, int nx2, uint32_t& mww,
@@ -800,7 +817,7 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
     if (ks == 0) {
       if (GATHER) {
         slot_load(r, c, t + 2);
-        slot_dma(c, t + 3);
+        slot_dma<CONTIG>(c, t + 3);
       }
     } else if (ks == 1) {
       alpha_load(a0, a1, alpha_t, c);
@@ -836,7 +853,7 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
 // iteration issues nothing else to global memory), P(t) and tile t's factors,
 // and frees stage t-1, P buffer t-1 and factors t-1 for reuse.  The softmax of
 // tile 0 runs ahead of the loop.
-template <bool WIDE, bool PRECISE>
+template <bool WIDE, bool PRECISE, bool CONTIG>
 __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds_u8* pbuf,
                                           bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
                                           float& m_ref, float& l_sum, float* alpha_s,
@@ -881,12 +898,12 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
     int resc;         // some row's reference moved in tile t
     bf16x8 A0[2];
     if (t + 2 < nt) {
-      S = qk_phase<WIDE, PRECISE, true>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww, ms.wb,
-                                        resc, A0, mb);
+      S = qk_phase<WIDE, PRECISE, true, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
+                                                ms.wb, resc, A0, mb);
       ms.valid = tile_valid(c, t + 1);
     } else if (t + 1 < nt) {
-      S = qk_phase<WIDE, PRECISE, false>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww, ms.wb,
-                                         resc, A0, mb);
+      S = qk_phase<WIDE, PRECISE, false, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
+                                                 ms.wb, resc, A0, mb);
       ms.valid = tile_valid(c, t + 1);
     } else {
       float a0, a1;
@@ -950,7 +967,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
 }
 
-template <bool WIDE, bool PRECISE, bool MASKB>
+template <bool WIDE, bool PRECISE, bool MASKB, bool CONTIG>
 __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
@@ -1016,6 +1033,10 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   c.wave = wave;
   c.lane = lane;
   c.scale_log2 = p.scale_log2;
+  // contiguous-prefix form: the request's first prefix entry names its run
+  // (nothing read past it; a request without prefix reads nothing here)
+  c.plen = CONTIG ? max(L - nq, 0) : 0;
+  c.run0 = (CONTIG && c.plen > 0) ? kv_indices_[k0] : 0;
   c.sring = sring_s + wave * (SLOT_RING * 256);
 
   const int i0 = row0 / H;
@@ -1069,7 +1090,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
 
   // prologue: the slot loads, then the query rows (their transfer overlaps the
   // slots' round trip), then the first two tiles' gathers
-  if (c.ntiles > 0) split_slots(c);
+  if (c.ntiles > 0) split_slots<CONTIG>(c);
 
   // query rows -> MFMA B operands (k = dims 16*ks + 8*half .. +7), all 576
   // dims in VGPRs for the whole split.  A row past the request's rows loads
@@ -1100,7 +1121,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
   if (c.ntiles > 0)
-    run_split<WIDE, PRECISE>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s, m0, mb);
+    run_split<WIDE, PRECISE, CONTIG>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s, m0, mb);
 
   // the last PV MFMAs must finish before O is read out of the AGPRs
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -1227,17 +1248,17 @@ hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
   void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mk, &mkp, &mw, &ord, &o, &l, &wo, &wl, &sc};
-  // [wide][precise][mask bytes]
-  static const void* const fns[2][2][2] = {
-      {{reinterpret_cast<const void*>(&tv_split_kernel<false, false, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<false, false, true>)},
-       {reinterpret_cast<const void*>(&tv_split_kernel<false, true, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<false, true, true>)}},
-      {{reinterpret_cast<const void*>(&tv_split_kernel<true, false, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<true, false, true>)},
-       {reinterpret_cast<const void*>(&tv_split_kernel<true, true, false>),
-        reinterpret_cast<const void*>(&tv_split_kernel<true, true, true>)}}};
-  const void* fn = fns[p.wide][p.precise][p.s.mask_bytes != 0];
+  // [wide][precise][mask bytes][contiguous prefix]
+#define TV_SPLIT_FN(W, P, M, C) reinterpret_cast<const void*>(&tv_split_kernel<W, P, M, C>)
+#define TV_SPLIT_FN2(W, P, M) {TV_SPLIT_FN(W, P, M, false), TV_SPLIT_FN(W, P, M, true)}
+#define TV_SPLIT_FN4(W, P) {TV_SPLIT_FN2(W, P, false), TV_SPLIT_FN2(W, P, true)}
+  static const void* const fns[2][2][2][2] = {
+      {TV_SPLIT_FN4(false, false), TV_SPLIT_FN4(false, true)},
+      {TV_SPLIT_FN4(true, false), TV_SPLIT_FN4(true, true)}};
+#undef TV_SPLIT_FN4
+#undef TV_SPLIT_FN2
+#undef TV_SPLIT_FN
+  const void* fn = fns[p.wide][p.precise][p.s.mask_bytes != 0][p.contig];
   if (ev0 || ev1) return hipExtLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st, ev0, ev1, 0);
   return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }

@@ -293,30 +293,35 @@ CONFIG_DESC = {
 CONFIG_SPLITS = {3: 32}
 
 
-def config(k: int, poison: bool = True) -> Workload:
+def config(k: int, poison: bool = True, placement: str = "random") -> Workload:
     rngs = _spawn(k)
     rt = rngs[0]
     if k == 1:
         prefix = [21]
         parents = [gen_tree(rt, 9)]
-        return build(k, prefix, parents, 8, 4096, poison=poison, name="C1")
+        return build(k, prefix, parents, 8, 4096, poison=poison, name="C1",
+                     placement=placement)
     if k == 2:
         prefix = [int(x) for x in rt.integers(512, 4097, size=8)]
         parents = [gen_tree(rt, 16, max_branch=4) for _ in range(8)]
-        return build(k, prefix, parents, 8, 65536, poison=poison, name="C2")
+        return build(k, prefix, parents, 8, 65536, poison=poison, name="C2",
+                     placement=placement)
     if k == 3:
         parents = [gen_tree(rt, 32, max_depth=8, max_branch=4)]
-        return build(k, [32768], parents, 16, 200000, poison=poison, name="C3")
+        return build(k, [32768], parents, 16, 200000, poison=poison, name="C3",
+                     placement=placement)
     if k == 4:
         parents = [gen_tree(rt, 64)]
-        return build(k, [200000], parents, 8, 262144, poison=poison, name="C4")
+        return build(k, [200000], parents, 8, 262144, poison=poison, name="C4",
+                     placement=placement)
     if k == 5:
         prefix = [int(round(math.exp(x))) for x in rt.uniform(math.log(256), math.log(65536), size=32)]
         parents = []
         for _ in range(32):
             d = int(rt.integers(3, 11))
             parents.append(gen_tree(rt, 24, max_depth=d))
-        return build(k, prefix, parents, 64, 524288, outlier_p=0.01, poison=poison, name="C5")
+        return build(k, prefix, parents, 64, 524288, outlier_p=0.01, poison=poison, name="C5",
+                     placement=placement)
     raise ValueError("unknown config %r" % k)
 
 
