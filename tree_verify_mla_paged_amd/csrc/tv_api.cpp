@@ -449,7 +449,11 @@ tv_status tv_append_draft(const tv_append_problem* p, const void* draft_kv,
 }
 
 const char* tv_status_str(tv_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the argument's bytes as one, since
+  // loading a value outside the enumerators as tv_status is undefined in C++
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case TV_OK: return "ok";
     case TV_ERR_NULL: return "a required pointer is NULL";
     case TV_ERR_SHAPE: return "a size in tv_problem is out of range or inconsistent";
