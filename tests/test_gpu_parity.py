@@ -565,6 +565,86 @@ def test_contiguous_prefix_pool_beyond_4gib(flags):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------- long splits over one row block
+
+def _plan_tiles(w, **kw):
+    from gpu_util import problem_for
+    pl = tv.plan(problem_for(w, **kw))
+    return pl, pl["split_keys"] // 32
+
+
+LONG_SHAPES = [
+    # seed, prefix lengths, draft counts, heads, num_splits: one row block (<= 128
+    # rows), splits of many tiles with ragged last splits
+    (801, [3000], [5], 8, 1),        # 94 tiles in one split
+    (802, [3000], [5], 8, 3),        # 32-tile splits, ragged last
+    (803, [3000], [5], 8, 12),       # 8-tile splits, last split 6 keys
+    (804, [2300], [9], 8, 9),        # 9-tile splits, last split 5 keys
+    (805, [8 * 32 * 4 - 5], [5], 3, 4),  # packed words at 3 heads; exactly 8 tiles each
+    (806, [3000, 2500, 17, 0], [5, 3, 2, 2], 16, 1),  # short and prefix-less requests
+    (807, [4000], [1], 128, 2),      # one draft x 128 heads: a full row block
+]
+
+
+@pytest.mark.parametrize("seed,prefix,ndraft,H,ns", LONG_SHAPES)
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_long_splits_one_row_block(seed, prefix, ndraft, H, ns, out_f32):
+    w = W.small(seed, prefix, ndraft, num_heads=H)
+    pl, tiles = _plan_tiles(w, num_splits=ns)
+    assert pl["row_blocks"] == 1 and tiles >= 8, pl
+    print("long split seed=%d H=%d ns=%d tiles/split=%d f32=%s" % (seed, H, ns, tiles, out_f32),
+          flush=True)
+    full_check(w, num_splits=ns, out_f32=out_f32, label="long%d" % seed)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_long_splits_in_every_form(flags):
+    """Precise mode, the contiguous-prefix form and the prefix-visible form, and
+    arbitrary (non-tree) masks, over long splits of one row block."""
+    base = W.small(808, [3100], [6], num_heads=8)
+    cont = W.contiguous_prefix_form(W.small(808, [3100], [6], num_heads=8,
+                                            placement="contiguous"))
+    pv = W.prefix_visible_form(base)
+    rnd = W.small(809, [2900], [7], num_heads=8)
+    rng = np.random.default_rng(809)
+    rnd.mask[:] = (rng.random(rnd.mask.size) < 0.4).astype(np.uint8)
+    for w in (base, cont, pv, rnd):
+        for ns in (1, 5):
+            print("long split form %s ns=%d flags=%d" % (w.name, ns, flags), flush=True)
+            full_check(w, num_splits=ns, out_f32=True, flags=flags,
+                       label="long %s ns=%d" % (w.name, ns))
+
+
+def test_s3_200k_every_row():
+    """S3 (9 drafts x 8 heads over 200k keys, 25-tile splits): every row, fp32
+    output at the literal bar."""
+    print("S3 every row", flush=True)
+    w = W.sweep(3)
+    ro, rl = oracle_full("S3", w)
+    o, l = run(w, out_f32=True)
+    st = compare(o, l, ro, rl, bf16_out=False, label="S3")
+    print("   %s" % st, flush=True)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_split_invariance_of_a_few_row_request(flags):
+    """S1 split 1, 4, 16 and 205 ways (1025, 257, 65 and 5 tiles per split):
+    lse within 1e-5, outputs within twice the probability-rounding bound."""
+    w = W.sweep(1)
+    tol_o = 2 * p_rounding_bound(w, precise=bool(flags)) + 1e-5
+    ref_o = ref_l = None
+    for ns in (1, 4, 16, 205):
+        print("S1 split invariance ns=%d flags=%d" % (ns, flags), flush=True)
+        g = GpuCall(w, num_splits=ns, out_f32=True, flags=flags)
+        g.call()
+        o, l = g.result()
+        if ref_o is None:
+            ref_o, ref_l = o, l
+            continue
+        assert float(np.abs(l - ref_l).max()) <= 1e-5, ns
+        assert (np.abs(o - ref_o) <= tol_o).all(), ns
+
+
 # ------------------------------ other workloads of the same kernels
 
 @pytest.mark.parametrize("H", [16, 128])
