@@ -952,6 +952,20 @@ __device__ __forceinline__ f16x8 to_f16x8(const f32x4& a, const f32x4& b) {
                (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 }
 
+// A 16-byte store at device scope (sc1): it is written through this XCD's L2 as
+// it happens, instead of staying there dirty until the kernel's end writes the L2
+// back (the partial outputs are 16-32 MB); the data still lands in the memory-
+// side cache, where the merge kernel reads it.  Measured: the split kernel's
+// end comes 2-3 us sooner at 32 MB of partials, the merge is unchanged.  A store
+// of more than 8 bytes reads its data registers after issue, and a VALU write to
+// them needs a wait state in between, which the compiler inserts only for
+// stores it can see: the s_nop is that wait.
+template <typename T>
+__device__ __forceinline__ void store_dev16(void* ptr, const T& v) {
+  static_assert(sizeof(T) == 16, "");
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(ptr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x4& a, const f32x4& b) {
   return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
                 (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
@@ -1194,7 +1208,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
           _Float16* o = static_cast<_Float16*>(ws_o_) + wi * VD + 8 * si;
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<f16x8*>(o + 64 * k) = to_f16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
+            store_dev16(o + 64 * k, to_f16x8(x[2 * k] * inv, x[2 * k + 1] * inv));
           if (si == 0) ws_lse_[2 * wi + 1] = (float)(e - 15);
         }
       } else if (live) {
@@ -1204,14 +1218,14 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
           o += 8 * si;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            *reinterpret_cast<f32x4*>(o + 64 * k) = x[2 * k] * inv;
-            *reinterpret_cast<f32x4*>(o + 64 * k + 4) = x[2 * k + 1] * inv;
+            store_dev16(o + 64 * k, f32x4(x[2 * k] * inv));
+            store_dev16(o + 64 * k + 4, f32x4(x[2 * k + 1] * inv));
           }
         } else {
           __bf16* o = static_cast<__bf16*>(out_) + gr * VD + 8 * si;
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<bf16x8*>(o + 64 * k) = to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
+            store_dev16(o + 64 * k, to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv));
         }
       }
       // the next row block into the other buffer (last read two blocks ago)
