@@ -954,9 +954,11 @@ __device__ __forceinline__ f16x8 to_f16x8(const f32x4& a, const f32x4& b) {
 
 // A 16-byte store at device scope (sc1): it is written through this XCD's L2 as
 // it happens, instead of staying there dirty until the kernel's end writes the L2
-// back (the partial outputs are 16-32 MB); the data still lands in the memory-
-// side cache, where the merge kernel reads it.  Measured: the split kernel's
-// end comes 2-3 us sooner at 32 MB of partials, the merge is unchanged.  A store
+// back; the data still lands in the memory-side cache, where the merge kernel
+// reads it.  Used for the fp16 partial outputs, where it was measured: the split
+// kernel's end comes 2-3 us sooner at 32 MB of partials, the merge unchanged.
+// (For the fp32 partials of precise mode, twice the bytes and stores, it made the
+// split kernel 20-40 % slower; those stay ordinary stores.)  A store
 // of more than 8 bytes reads its data registers after issue, and a VALU write to
 // them needs a wait state in between, which the compiler inserts only for
 // stores it can see: the s_nop is that wait.
@@ -1218,14 +1220,14 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
           o += 8 * si;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            store_dev16(o + 64 * k, f32x4(x[2 * k] * inv));
-            store_dev16(o + 64 * k + 4, f32x4(x[2 * k + 1] * inv));
+            *reinterpret_cast<f32x4*>(o + 64 * k) = x[2 * k] * inv;
+            *reinterpret_cast<f32x4*>(o + 64 * k + 4) = x[2 * k + 1] * inv;
           }
         } else {
           __bf16* o = static_cast<__bf16*>(out_) + gr * VD + 8 * si;
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            store_dev16(o + 64 * k, to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv));
+            *reinterpret_cast<bf16x8*>(o + 64 * k) = to_bf16x8(x[2 * k] * inv, x[2 * k + 1] * inv);
         }
       }
       // the next row block into the other buffer (last read two blocks ago)
