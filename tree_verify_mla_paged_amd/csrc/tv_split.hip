@@ -454,17 +454,49 @@ struct Soft {
   bf16x8 pk[2], pl[2];   // P^T operands of k-steps 0 and 1 (lo: precise mode)
 };
 
-// mask, max of keys 0-7, of 8-15, row max, reference x3, 8 probability pairs
-// in three steps each (exponents, exponentials, sum and bf16 pair), the P write:
-// one step per PV MFMA
+// mask, max of keys 0-7, of 8-15, row max, reference x3; the exponents of
+// probability pair 0; per pair p = 0..7 its two exponentials (step A), then the
+// exponents of pair p+1 followed by pair p's sum and bf16 pack (step B); the P
+// write: one step per PV MFMA.  The order inside step B keeps an independent
+// instruction between each transcendental and the first instruction reading
+// its result, and between each exponent and the exponential reading it: the
+// hardware needs one wait state there, and an MFMA written as inline asm does
+// not count as one for the compiler, which would pad with s_nop instead.
 constexpr int SOFT_PRE = 7;
-constexpr int SOFT_STEPS = SOFT_PRE + 3 * 8 + 1;
+constexpr int SOFT_STEPS = SOFT_PRE + 1 + 2 * 8 + 1;
 
 // v_max3_f32 as written: the fmaxf library form first quiets each input (an
 // extra instruction per value); the scores are finite or -inf.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// The maximum of 8 values in one asm block: dependent VALU instructions inside
+// a block need no wait states, where the compiler pads between separate
+// statements whose operands a VALU instruction just wrote.
+__device__ __forceinline__ float max8f(float a0, float a1, float a2, float a3, float a4, float a5,
+                                      float a6, float a7) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3\n\t"
+      "v_max3_f32 %0, %0, %4, %5\n\t"
+      "v_max3_f32 %0, %0, %6, %7\n\t"
+      "v_max_f32 %0, %0, %8"
+      : "=&v"(r)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4), "v"(a5), "v"(a6), "v"(a7));
+  return r;
+}
+// max(m, |a_i|, |b_i|) over two 4-vectors: absolute values as source modifiers
+// (no separate instruction per value), one block as above.
+__device__ __forceinline__ float max_abs8(float m, const f32x4& a, const f32x4& b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|\n\t"
+      "v_max3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_max3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_max3_f32 %0, %0, |%8|, |%9|"
+      : "=&v"(r)
+      : "v"(m), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]),
+        "v"(b[3]));
   return r;
 }
 
@@ -503,10 +535,8 @@ __device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, MaskSel
   } else if (step == 1 || step == 2) {
     fence(S);
     const int o = 8 * (step - 1);
-    float m = max3f(S[o], S[o + 1], S[o + 2]);
-    m = max3f(m, S[o + 3], S[o + 4]);
-    m = max3f(m, S[o + 5], S[o + 6]);
-    m = max3f(m, S[o + 7], S[o + 7]);
+    const float m = max8f(S[o], S[o + 1], S[o + 2], S[o + 3], S[o + 4], S[o + 5], S[o + 6],
+                          S[o + 7]);
     if (step == 1) {
       sm.ma = m;
       fence(sm.ma);
@@ -552,23 +582,31 @@ __device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, MaskSel
   } else if (step == SOFT_STEPS - 1) {
     write_p<PRECISE>(pb_u, c, sm);
   } else {
-    // probabilities i, i+1 (one packed bf16 pair)
-    const int j = step - SOFT_PRE, i = 2 * (j / 3);
-    if (j % 3 == 0) {
-      float x0 = S[i], x1 = S[i + 1];
+    // probability pairs: keys i, i+1 of pair p = i / 2 (one packed bf16 pair)
+    const int j = step - SOFT_PRE;
+    const int p = j == 0 ? 0 : (j - 1) / 2;
+    const bool step_a = j > 0 && (j - 1) % 2 == 0;
+    const int i = 2 * p;
+    // the exponents of pair q
+    auto exponents = [&](int q) {
+      float x0 = S[2 * q], x1 = S[2 * q + 1];
       fence(x0);
       fence(x1);
       sm.y0 = __builtin_fmaf(x0, c.scale_log2, -sm.mu);
       sm.y1 = __builtin_fmaf(x1, c.scale_log2, -sm.mu);
       fence(sm.y0);
       fence(sm.y1);
-    } else if (j % 3 == 1) {
+    };
+    if (j == 0) {
+      exponents(0);
+    } else if (step_a) {
       fence(sm.y1);
       sm.e0 = __builtin_amdgcn_exp2f(sm.y0);
       sm.e1 = __builtin_amdgcn_exp2f(sm.y1);
       fence(sm.e0);
       fence(sm.e1);
     } else {
+      if (p + 1 < 8) exponents(p + 1);
       fence(sm.e1);
       l_sum += sm.e0;
       l_sum += sm.e1;
@@ -1193,10 +1231,13 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
         // row's max |o| < 2^e, o * 2^(15 - e) stays below 2^15 (no overflow,
         // values down to 2^-29 of the max stay normal); o = h * 2^(e - 15).
         // The scale folds into the 1/l multiply.
-        float m = 0.f;
+        float m = 0.f, m2 = 0.f;  // two independent chains
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          m = max3f(m, max3f(fabsf(x[k][0]), fabsf(x[k][1]), fabsf(x[k][2])), fabsf(x[k][3]));
+        for (int k = 0; k < 8; k += 2) {
+          m = max_abs8(m, x[k], x[k + 1]);
+          m2 = max_abs8(m2, x[k + 8], x[k + 9]);
+        }
+        m = max3f(m, m2, m2);
         float d = dpp_f<0xb1>(m);  // the 8 lanes of the row: pairs, quads, halves of 8
         m = max3f(m, d, d);
         d = dpp_f<0x4e>(m);
