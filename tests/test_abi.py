@@ -345,3 +345,25 @@ def test_static_entry_point_rejects_plans_beyond_its_scratch():
     assert tv.verify_attn_static_status(prob(), *args, float("nan"), fake, fake) == 2
     p0 = prob(batch=0, total_q=0, max_q_len=0)
     assert tv.verify_attn_static_status(p0, 0, 0, 0, 0, 0, 0, 0, 0.07, 0, 0) == 0
+
+
+def test_build_refuses_kernels_that_spill():
+    """The build reads hipcc's per-kernel resource remarks and refuses a kernel
+    with scratch or spilled VGPRs (every build runs that check): the parser on a
+    sample with one clean and one spilling kernel."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "tv_build", os.path.join(ROOT, "tree_verify_mla_paged_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    sample = "\n".join([
+        "a.hip:1:1: remark: Function Name: _ZN2tv1kE [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 150 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: _ZN2tv1jE [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 832 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     VGPRs Spill: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert b.resource_usage(sample) == [("_ZN2tv1kE", 0, 0), ("_ZN2tv1jE", 832, 12)]
+    assert b.resource_usage("") == []
