@@ -180,13 +180,31 @@ def test_random_masks_many_splits():
 
 # ------------------------------------------------- split-count invariance
 
+def check_split_drift(o, l, ref_o, ref_l, tol_o, label):
+    """Two split counts of one problem: lse within 1e-5; every output within
+    twice the bound on the probability rounding (each run is within it of the
+    exact result) plus 1e-5 for fp32 accumulation order; and the mean drift
+    within 1/100 of that: the bound assumes every rounding error of the
+    probabilities aligned, which independent roundings do not (measured at C3
+    and S1, both modes: mean drift 0.0008-0.0012 of twice the bound, largest
+    single value 0.048), so a drift common to many outputs stands out."""
+    dl = float(np.abs(l - ref_l).max())
+    do = np.abs(o - ref_o)
+    ratio = float(np.mean(do / np.broadcast_to(tol_o, do.shape)))
+    print("   %s: max |dlse| %.3g  max |dout| %.3g  mean |dout| / tol %.3g"
+          % (label, dl, float(do.max()), ratio), flush=True)
+    assert dl <= 1e-5, label
+    assert (do <= tol_o).all(), label
+    assert ratio <= 0.01, label
+
+
 @pytest.mark.parametrize("flags", [0, 1])
 def test_split_count_invariance(flags):
-    """lse within 1e-5 for every split count; outputs within twice the bound on
-    the probability rounding (each run is within it of the exact result) plus
-    1e-5 for fp32 accumulation order."""
+    """Every split count of C3 against the oracle at the parity bar (sampled
+    rows), and against the single split (all rows, check_split_drift)."""
     w = W.config(3)
     rows = sample_rows(w, 64, seed=3)
+    ro, rl = oracle.run(w, rows=rows)
     tol_o = 2 * p_rounding_bound(w, precise=bool(flags)) + 1e-5
     ref_o = ref_l = None
     for ns in (1, 2, 3, 7, 16, 32, 64, 128):
@@ -196,16 +214,11 @@ def test_split_count_invariance(flags):
         o, l = g.result()
         o = o.reshape(-1, 512)
         l = l.reshape(-1)
+        compare(o[rows], l[rows], ro, rl, bf16_out=False, label="C3 ns=%d" % ns)
         if ref_o is None:
             ref_o, ref_l = o, l
-            ro, rl = oracle.run(w, rows=rows)
-            compare(o[rows], l[rows], ro, rl, bf16_out=False, label="C3 ns=1")
             continue
-        dl = float(np.abs(l - ref_l).max())
-        do = np.abs(o - ref_o)
-        print("   max |dlse| %.3g  max |dout| %.3g" % (dl, float(do.max())), flush=True)
-        assert dl <= 1e-5, ns
-        assert (do <= tol_o).all(), ns
+        check_split_drift(o, l, ref_o, ref_l, tol_o, "ns=%d" % ns)
 
 
 # ------------------------------------------------------ exact visibility
@@ -629,8 +642,11 @@ def test_s3_200k_every_row():
 @pytest.mark.parametrize("flags", [0, 1])
 def test_split_invariance_of_a_few_row_request(flags):
     """S1 split 1, 4, 16 and 205 ways (1025, 257, 65 and 5 tiles per split):
-    lse within 1e-5, outputs within twice the probability-rounding bound."""
+    each against the oracle at the parity bar (sampled rows), and against the
+    single split (check_split_drift)."""
     w = W.sweep(1)
+    rows = sample_rows(w, 24, seed=5)
+    ro, rl = oracle.run(w, rows=rows)
     tol_o = 2 * p_rounding_bound(w, precise=bool(flags)) + 1e-5
     ref_o = ref_l = None
     for ns in (1, 4, 16, 205):
@@ -638,11 +654,13 @@ def test_split_invariance_of_a_few_row_request(flags):
         g = GpuCall(w, num_splits=ns, out_f32=True, flags=flags)
         g.call()
         o, l = g.result()
+        o = o.reshape(-1, 512)
+        l = l.reshape(-1)
+        compare(o[rows], l[rows], ro, rl, bf16_out=False, label="S1 ns=%d" % ns)
         if ref_o is None:
             ref_o, ref_l = o, l
             continue
-        assert float(np.abs(l - ref_l).max()) <= 1e-5, ns
-        assert (np.abs(o - ref_o) <= tol_o).all(), ns
+        check_split_drift(o, l, ref_o, ref_l, tol_o, "ns=%d" % ns)
 
 
 # ------------------------------ other workloads of the same kernels
