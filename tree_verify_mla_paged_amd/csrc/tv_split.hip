@@ -68,7 +68,7 @@ constexpr int ROW = 1088;                 // LDS row pitch of a key's latent dim
 constexpr int MAIN_BYTES = 34816;         // 32 rows at ROW plus the largest key_shift, 256-aligned
 constexpr int ROPE_BYTES = TILE * 128;    // RoPE dims 512..575 of 32 keys
 constexpr int MASKW_BYTES = 4 * 64 * 4;   // 256 visibility words (one per draft)
-constexpr int STAGE = MAIN_BYTES + ROPE_BYTES + MASKW_BYTES;  // 46080
+constexpr int STAGE = MAIN_BYTES + ROPE_BYTES + MASKW_BYTES;  // 39936
 constexpr int NSTAGE = 3;
 constexpr int DMA_PER_TILE = 10;          // direct-to-LDS loads per wave per tile
 constexpr int SLOT_RING = 4;              // tiles of gather slots held per wave in LDS
