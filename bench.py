@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -155,11 +156,21 @@ def algorithmic(w):
     return kv_bytes, total_bytes, flops
 
 
+def code_text(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed: what
+    the compiler sees of it (the kernel sources hold no string with // or /*)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def source_hash():
-    """The split kernel's source and the parameter structs it is launched with."""
+    """The split kernel's code and the parameter structs it is launched with
+    (comments and layout excluded)."""
     h = hashlib.sha256()
     for f in ("tv_split.hip", "tv_kernels.h"):
-        h.update(open(os.path.join(ROOT, "tree_verify_mla_paged_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "tree_verify_mla_paged_amd", "csrc", f)).read()
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -66,3 +66,14 @@ def test_contiguous_prefix_workload_and_counts():
     _, tot_c, fl_c = bench.algorithmic(w)
     _, tot_f, fl_f = bench.algorithmic(full)
     assert fl_c == fl_f and tot_f - tot_c == 4 * 32767
+
+
+def test_traffic_key_ignores_comments_not_code():
+    """The counter summary is keyed on the split kernel's code: a comment or
+    layout change keeps the key, a changed token does not."""
+    a = "int f(int x) {  // one\n  return x + 1;  /* two\n lines */\n}\n"
+    b = "int f(int x) {\n  // another comment\n  return x + 1;\n}"
+    c = "int f(int x) {\n  return x + 2;\n}"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert len(bench.source_hash()) == 16
