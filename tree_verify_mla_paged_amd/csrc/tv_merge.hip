@@ -18,9 +18,10 @@ namespace tv {
 // One workgroup of 256 threads per (row, slice of VD / DS value dims), in
 // chunks of up to MERGE_CHUNK splits.  DS = 4 spreads the rows of a small
 // problem over four times as many compute units (each reads a quarter of every
-// partial row; the weights are recomputed per slice).  A thread's first U
-// partial-output loads go out before anything else; meanwhile the chunk's
-// split LSEs are read once, cooperatively, and turned into weights in LDS.
+// partial row; the weights are recomputed per slice).  A chunk's split LSEs
+// are read first, once, cooperatively; then a thread's first U partial-output
+// loads go out, and while they are in flight the LSEs are turned into weights
+// in LDS, so that each partial is accumulated as it lands.
 // Each load is 16 bytes: a thread owns DPT value dims (8 fp16 or 4 fp32), so a
 // split's slice takes TPS threads and the workgroup's NPH = 256 / TPS phases
 // take alternate splits, combined through LDS at the end: NPH * U splits are
@@ -80,24 +81,41 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
   f16x8 vh[U];
   // the partial outputs of splits c0 + s0 + NPH*j: every split below ns was
   // written by the split kernel (an empty one as zeros), so these loads need
-  // no weight and go out before the weights are known
+  // no weight and go out before the weights are known.  A split past ns loads
+  // split ns - 1 again, with weight 0 below: the loads are unconditional, so
+  // the compiler counts them exactly when it waits for the older LSE loads (a
+  // load under a branch makes it wait for every load in flight).
   auto load_batch = [&](int c0, int s0) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int s = c0 + s0 + NPH * j;
-      if (F16P) vh[j] = s < ns ? *reinterpret_cast<const f16x8*>(ph + (int64_t)s * VD) : f16x8{};
-      else v[j] = s < ns ? *reinterpret_cast<const f32x4*>(po + (int64_t)s * VD) : f32x4{};
+      const int s = min(c0 + s0 + NPH * j, ns - 1);
+      if (F16P) vh[j] = *reinterpret_cast<const f16x8*>(ph + (int64_t)s * VD);
+      else v[j] = *reinterpret_cast<const f32x4*>(po + (int64_t)s * VD);
     }
   };
+  constexpr int PER = MERGE_CHUNK / NT;  // a thread's share of a chunk's splits
   for (int c0 = 0; c0 < ns; c0 += MERGE_CHUNK) {
     const int nc = min(MERGE_CHUNK, ns - c0);
+    // the chunk's split LSEs (and scale exponents) go out first: vector loads
+    // return in issue order, so behind the partial rows they would wait for
+    // all of them, and no accumulation could start before the last row landed
+    // (unconditional loads of a clamped split, then a select: a load under a
+    // branch would be followed by a wait for every load in flight)
+    float lvs[PER], kxs[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = t + NT * u;
+      const int ic = c0 + min(i, nc - 1);
+      const float lv = ls[LS * ic];
+      const float kx = F16P ? ls[LS * ic + 1] : 0.f;
+      lvs[u] = i < nc ? lv : -INFINITY;
+      kxs[u] = i < nc ? kx : 0.f;
+    }
+    asm volatile("" ::: "memory");  // (issue order)
     load_batch(c0, h);
     float m = -INFINITY;
-    for (int i = t; i < nc; i += NT) {
-      const float lv = ls[LS * (c0 + i)];
-      wgt_s[i] = lv;
-      m = fmaxf(m, lv);
-    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) m = fmaxf(m, lvs[u]);
     const float Mn = fmaxf(M, block_max(m, red));
     if (Mn == -INFINITY) continue;  // every split so far is empty (uniform)
     if (Mn > M) {
@@ -107,10 +125,14 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
       W *= f;
       M = Mn;
     }
-    for (int i = t; i < nc; i += NT) {
-      const float w = __expf(wgt_s[i] - M);  // exp(-inf) = 0
-      wgt_s[i] = w;
-      if (F16P) wnum_s[i] = __builtin_ldexpf(w, (int)ls[LS * (c0 + i) + 1]);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = t + NT * u;
+      if (i < nc) {
+        const float w = __expf(lvs[u] - M);  // exp(-inf) = 0
+        wgt_s[i] = w;
+        if (F16P) wnum_s[i] = __builtin_ldexpf(w, (int)kxs[u]);
+      }
     }
     __syncthreads();
     for (int s0 = h; s0 < nc; s0 += NPH * U) {
@@ -184,23 +206,34 @@ __global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
   const int LS = F16P ? 2 : 1;
   const float* ls = p.ws_lse + g * p.max_splits * LS;
   const int d = lane * 8;
+  // lane s's split lse and scale exponent first (vector loads return in issue
+  // order: behind the partial rows they would wait for all of them)
+  // (a clamped split loaded unconditionally, then a select: a load under a
+  // branch would be followed by a wait for every load in flight)
+  const int sc = min(lane, ns - 1);
+  const float lv0 = ls[LS * sc];
+  const float kx0 = F16P ? ls[LS * sc + 1] : 0.f;
+  const float lv = lane < ns ? lv0 : -INFINITY;
+  const float kx = lane < ns ? kx0 : 0.f;
+  asm volatile("" ::: "memory");  // (issue order)
   f16x8 vh[MS];
   f32x4 v0[MS], v1[MS];
+  // (a split past ns loads split ns - 1 again and is not used: unconditional
+  // loads, counted exactly by the compiler's waits, as in tv_merge_kernel)
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
-    if (s < ns) {
-      if (F16P) {
-        vh[s] = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.ws_o) +
-                                                (g * p.max_splits + s) * VD + d);
-      } else {
-        const float* po = static_cast<const float*>(p.ws_o) + (g * p.max_splits + s) * VD + d;
-        v0[s] = *reinterpret_cast<const f32x4*>(po);
-        v1[s] = *reinterpret_cast<const f32x4*>(po + 4);
-      }
+    const int sl = min(s, ns - 1);
+    if (F16P) {
+      vh[s] = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.ws_o) +
+                                              (g * p.max_splits + sl) * VD + d);
+    } else {
+      const float* po = static_cast<const float*>(p.ws_o) + (g * p.max_splits + sl) * VD + d;
+      v0[s] = *reinterpret_cast<const f32x4*>(po);
+      v1[s] = *reinterpret_cast<const f32x4*>(po + 4);
     }
   }
-  const float lv = lane < ns ? ls[LS * lane] : -INFINITY;
-  const float kx = (F16P && lane < ns) ? ls[LS * lane + 1] : 0.f;
+  // the reductions below wait for the lse: keep them after the row loads
+  __builtin_amdgcn_sched_barrier(0);
   float M = lv;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
