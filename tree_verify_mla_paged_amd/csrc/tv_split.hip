@@ -966,18 +966,37 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
   __syncthreads();
 }
 
-// Epilogue helpers.  O^T of row block RB (accumulators O[4*db + RB]) into the
-// staging region of this lane's row: dims 32*db + 8*(r/4) + 4*half + r%4.
+// Epilogue helpers.  The staging layout: row r of a wave's region is 512 bytes
+// (its 128 dims in fp32), the 16-byte granule g (dims 4g..4g+3 of the slice)
+// at slot g ^ r.  The writes go down a column (one granule of 32 rows) and the
+// reads along rows (8 lanes a row, every other granule); with the XOR both
+// spread over all banks.  A slot address is the lane's base XOR a constant:
+// the base holds the row's 512-aligned offset and the lane's own bits of the
+// slot, the constant the granule bits the instruction picks.
+//
+// O^T of row block RB (accumulators O[4*db + RB]) into the staging region:
+// this lane's row r, granules 8*db + 2*q + half (dims 32*db + 8*q + 4*half +
+// 0..3, the accumulator's elements 4q..4q+3).  `base` = region offset + 512*r
+// + 16*(half ^ r).
 template <int RB>
-__device__ __forceinline__ void stage_rows(lds_u8* ep, const f32x16 (&O)[16]) {
+__device__ __forceinline__ void stage_rows(lds_u8* buf, uint32_t base, const f32x16 (&O)[16]) {
+  // The 16 addresses are formed here, beside the writes (which the LDS write
+  // rate bounds), not hoisted ahead of the barrier before the first block.  The
+  // writes are asm so that the compiler does not merge the row blocks' copies
+  // of this code, which would route the accumulators through VGPRs.
+  asm volatile("" : "+v"(base));
+  const uint32_t b0 = (uint32_t)(uintptr_t)buf;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x16& o = O[4 * db + RB];
-      *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(ep + 128 * db + 32 * q) =
-          f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+      const f32x4 v = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+      asm volatile("ds_write_b128 %0, %1" : : "v"(b0 + (base ^ (128 * db + 32 * q))), "a"(v) : "memory");
     }
+  // the compiler does not count asm LDS writes: it would drop the wait that
+  // the barrier after every staging needs
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 template <int CTRL>
@@ -1196,33 +1215,35 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   __syncthreads();
 
   // O^T -> LDS -> global, one row block (32 rows) at a time: wave w puts its
-  // 128 dims of the 32 rows into region w ([32 rows][EP_ROW bytes]); then 8
-  // lanes store each row: lane i of a row covers dims 64k + 8i .. +7, k = 0..7,
-  // so that each store instruction writes whole contiguous row segments.  Two
-  // staging buffers: the row block after the current one is staged while the
-  // current one's stores drain.  The row-block loop is rolled (this code runs
-  // once per workgroup).
-  constexpr int EP_ROW = 528;  // 512 bytes of a row's 128 dims, + 16: conflict-free writes
+  // 128 dims of the 32 rows into region w ([32 rows][512 bytes], granules
+  // XOR-swizzled by row as described at stage_rows); then 8 lanes store each
+  // row: lane i of a row covers dims 64k + 8i .. +7, k = 0..7, so that each
+  // store instruction writes whole contiguous row segments.  Two staging
+  // buffers: the row block after the current one is staged while the current
+  // one's stores drain.  The row-block loop is rolled (this code runs once per
+  // workgroup).
+  constexpr int EP_ROW = 512;
   constexpr int EPB = 4 * 32 * EP_ROW;
   static_assert(2 * EPB <= NSTAGE * STAGE + PB2, "");
   {
-    lds_u8* ep = stages + wave * 32 * EP_ROW + l32 * EP_ROW + 16 * half;
+    const uint32_t wbase = (uint32_t)(wave * 32 * EP_ROW + l32 * EP_ROW + 16 * (half ^ l32));
     const int lr = tid >> 3, si = tid & 7;       // row within the row block, lane in the row
     const int nrb = min(4, (R - row0 + 31) >> 5);  // row blocks holding a row of the request
-    stage_rows<0>(ep, O);
+    stage_rows<0>(stages, wbase, O);
     __syncthreads();
 #pragma unroll 1
     for (int rb = 0; rb < nrb; ++rb) {
-      const lds_u8* rd = stages + (rb & 1) * EPB + lr * EP_ROW + 32 * si;  // chunk k = 0
+      // chunk k (dims 64k + 8*si .. +7) is region k/2, granules 16*(k&1) +
+      // 2*si + {0, 1} of row lr
+      const uint32_t rbase = (uint32_t)((rb & 1) * EPB + lr * EP_ROW + 16 * ((2 * si) ^ lr));
       const int rl = 32 * rb + lr;  // row within the workgroup's block
-      // chunk k: dims 64k + 8*si: region k/2, byte offset 256*(k&1) + 32*si
       f32x4 x[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const lds_u8* c0 = rd + (k >> 1) * 32 * EP_ROW + 256 * (k & 1);
-        x[2 * k] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(c0);
-        x[2 * k + 1] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(c0 + 16);
-      }
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          x[2 * k + h] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              stages + (rbase ^ (256 * (k & 1) + 16 * h)) + (k >> 1) * 32 * EP_ROW);
       float inv = inv_s[rl];
       const int64_t gr = (int64_t)q0 * H + row0 + rl;
       const bool live = row0 + rl < R;
@@ -1273,9 +1294,9 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
       }
       // the next row block into the other buffer (last read two blocks ago)
       switch (rb + 1 < nrb ? rb : 3) {
-        case 0: stage_rows<1>(ep + EPB, O); break;
-        case 1: stage_rows<2>(ep, O); break;
-        case 2: stage_rows<3>(ep + EPB, O); break;
+        case 0: stage_rows<1>(stages, wbase + EPB, O); break;
+        case 1: stage_rows<2>(stages, wbase, O); break;
+        case 2: stage_rows<3>(stages, wbase + EPB, O); break;
         default: break;
       }
       __syncthreads();
