@@ -201,13 +201,16 @@ def check_split_drift(o, l, ref_o, ref_l, tol_o, label):
 @pytest.mark.parametrize("flags", [0, 1])
 def test_split_count_invariance(flags):
     """Every split count of C3 against the oracle at the parity bar (sampled
-    rows), and against the single split (all rows, check_split_drift)."""
+    rows), and against the single split (all rows, check_split_drift).  The
+    counts take each merge form at its edges: the per-row merge (up to 32 fp16
+    or 16 fp32 splits) issues 4, 8, 16 or 32 loads per row, the per-workgroup
+    merge takes the rest."""
     w = W.config(3)
     rows = sample_rows(w, 64, seed=3)
     ro, rl = oracle.run(w, rows=rows)
     tol_o = 2 * p_rounding_bound(w, precise=bool(flags)) + 1e-5
     ref_o = ref_l = None
-    for ns in (1, 2, 3, 7, 16, 32, 64, 128):
+    for ns in (1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 32, 33, 64, 128):
         print("C3 split invariance ns=%d flags=%d" % (ns, flags), flush=True)
         g = GpuCall(w, num_splits=ns, out_f32=True, flags=flags)
         g.call()

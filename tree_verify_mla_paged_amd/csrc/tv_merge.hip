@@ -190,38 +190,30 @@ __global__ __launch_bounds__(NT) void tv_merge_kernel(MergeParams p) {
 // before the weights are known; the weights come from wave reductions, with no
 // LDS and no barrier.  Same arithmetic as tv_merge_kernel: M = max_s lse_s,
 // w_s = exp(lse_s - M), out = sum_s w_s 2^k_s h_s / sum_s w_s, lse = M + ln sum_s w_s.
-template <int OUT, bool F16P>
-__global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
-  constexpr int MS = merge_wave_splits(F16P);
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);  // wave-uniform
-  const int q0 = p.qo_indptr[b];
-  const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
-  if (r >= R) return;
-  const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
-  const int ns = min(min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, MS), p.max_splits);
-  if (ns <= 1) return;  // written directly by the split kernel
-  const int64_t g = (int64_t)q0 * p.num_heads + r;
+//
+// The loads are unconditional (a split past ns loads split ns - 1 again and is
+// not used), so that the compiler's waits count them exactly: a load under a
+// branch is followed by a wait for every load in flight.  CAP, the number
+// issued, is the smallest of 4, 8, 16, 32 that holds ns (one instantiation
+// each, chosen by a branch that is uniform over the workgroup: its rows share
+// a request), so a row of few splits issues few loads.
+template <int OUT, bool F16P, int CAP>
+__device__ __forceinline__ void merge_row(const MergeParams& p, int64_t g, int ns, int lane) {
   const int LS = F16P ? 2 : 1;
   const float* ls = p.ws_lse + g * p.max_splits * LS;
   const int d = lane * 8;
   // lane s's split lse and scale exponent first (vector loads return in issue
   // order: behind the partial rows they would wait for all of them)
-  // (a clamped split loaded unconditionally, then a select: a load under a
-  // branch would be followed by a wait for every load in flight)
   const int sc = min(lane, ns - 1);
   const float lv0 = ls[LS * sc];
   const float kx0 = F16P ? ls[LS * sc + 1] : 0.f;
   const float lv = lane < ns ? lv0 : -INFINITY;
   const float kx = lane < ns ? kx0 : 0.f;
   asm volatile("" ::: "memory");  // (issue order)
-  f16x8 vh[MS];
-  f32x4 v0[MS], v1[MS];
-  // (a split past ns loads split ns - 1 again and is not used: unconditional
-  // loads, counted exactly by the compiler's waits, as in tv_merge_kernel)
+  f16x8 vh[CAP];
+  f32x4 v0[CAP], v1[CAP];
 #pragma unroll
-  for (int s = 0; s < MS; ++s) {
+  for (int s = 0; s < CAP; ++s) {
     const int sl = min(s, ns - 1);
     if (F16P) {
       vh[s] = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.ws_o) +
@@ -248,7 +240,7 @@ __global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
     for (int o = 32; o > 0; o >>= 1) W += __shfl_xor(W, o);
     const float wn = F16P ? __builtin_ldexpf(w, (int)kx) : w;
 #pragma unroll
-    for (int s = 0; s < MS; ++s) {
+    for (int s = 0; s < CAP; ++s) {
       if (s < ns) {
         const float ws = __shfl(wn, s);
 #pragma unroll
@@ -272,6 +264,26 @@ __global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[e];
     *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(p.out) + g * VD + d) = o;
   }
+}
+
+template <int OUT, bool F16P>
+__global__ __launch_bounds__(NT) void tv_merge_rows_kernel(MergeParams p) {
+  constexpr int MS = merge_wave_splits(F16P);
+  static_assert(MS == 16 || MS == 32, "");
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);  // wave-uniform
+  const int q0 = p.qo_indptr[b];
+  const int R = (p.qo_indptr[b + 1] - q0) * p.num_heads;
+  if (r >= R) return;
+  const int L = p.kv_indptr[b + 1] - p.kv_indptr[b];
+  const int ns = min(min(L > 0 ? (L + p.split_keys - 1) / p.split_keys : 1, MS), p.max_splits);
+  if (ns <= 1) return;  // written directly by the split kernel
+  const int64_t g = (int64_t)q0 * p.num_heads + r;
+  if (ns <= 4) merge_row<OUT, F16P, 4>(p, g, ns, lane);
+  else if (ns <= 8) merge_row<OUT, F16P, 8>(p, g, ns, lane);
+  else if (MS == 16 || ns <= 16) merge_row<OUT, F16P, 16>(p, g, ns, lane);
+  else merge_row<OUT, F16P, MS>(p, g, ns, lane);
 }
 
 hipError_t launch_merge_rows(const MergeParams& p, int rows, int batch, int out, bool f16_parts,
