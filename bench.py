@@ -437,6 +437,44 @@ def warm_times(call, ev, stream, n):
             "split_kernel_timed_launches": len(split)}
 
 
+def clean_cold_times(call, ev, stream, n):
+    """Secondary figure: caches cold but clean.  Before each call a reduction
+    reads a 1 GiB buffer that was written once, before any of these calls (the
+    timed steps' scrub writes instead: the dirty lines it leaves in the MALL
+    are written back while the call reads, which for a call that mostly reads
+    adds about as much HBM traffic as the call's own).  Even calls are
+    bracketed by events on the stream, odd calls carry the split kernel's own
+    event pair, as in the timed steps."""
+    import torch
+    rbuf = torch.ones(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
+    n_call = (n + 1) // 2
+    pairs = [(ev.create(), ev.create()) for _ in range(n // 2)]
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_call)]
+    with torch.cuda.stream(stream):
+        rbuf.sum()  # its own fill's dirty lines leave the MALL here
+        for _ in range(3):
+            rbuf.sum()
+            call()
+        for i in range(n):
+            rbuf.sum()
+            if i % 2 == 0:
+                calls[i // 2][0].record(stream)
+                call()
+                calls[i // 2][1].record(stream)
+            else:
+                call(pairs[i // 2])
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in calls]
+    split = [ev.elapsed_ms(a, b) * 1e3 for a, b in pairs] or [float("nan")]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    del rbuf
+    return {"calls_bracketed": len(us), "us_per_call": float(np.median(us)),
+            "split_kernel_avg_us": float(np.mean(split)), "split_kernel_timed_launches": len(pairs)}
+
+
 def graph_times(call, stream, n):
     """The call captured into a HIP graph: wall clock over n replays back to
     back, and 50 replays each bracketed by events outside the graph."""
@@ -642,10 +680,11 @@ def main():
     ms_per_step = float(np.median(call_us)) * 1e-3
     timed_region_s = t1 - t0
 
-    warm = None
+    warm = clean = None
     graph_us = graph_events = None
     if not args.timed_only:
         warm = warm_times(call, ev, stream, max(args.steps, 50))
+        clean = clean_cold_times(call, ev, stream, max(args.steps, 20))
         graph_us, graph_events = graph_times(call, stream, max(args.steps, 50))
 
     append = append_times(w, args.steps, args.prefix_visible) if args.append else None
@@ -683,6 +722,12 @@ def main():
             warm["split_kernel_avg_us"] * 1e-6) / (1e12 if roof["bound"] == "mfma" else 1e9)
         roof["warm"] = {"kernel_avg_us": warm["split_kernel_avg_us"], "achieved": w_ach,
                         "frac": w_ach / roof["peak"]}
+    if clean:
+        # and cold caches holding no dirty lines (see clean_cold_times)
+        c_ach = (flops if roof["bound"] == "mfma" else total_bytes) / (
+            clean["split_kernel_avg_us"] * 1e-6) / (1e12 if roof["bound"] == "mfma" else 1e9)
+        roof["clean_cold"] = {"kernel_avg_us": clean["split_kernel_avg_us"], "achieved": c_ach,
+                              "frac": c_ach / roof["peak"]}
     roof["algorithmic"] = {"bytes": total_bytes, "flops": flops,
                            "floor_us": max(t_hbm, t_mfma) * 1e6}
     if calib:
@@ -698,7 +743,8 @@ def main():
         "us_per_call": us_per_call, "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "timing": ("value, ms_per_step and us_per_call: median over the even timed steps of "
                    "the event-bracketed call, each step after a %d-byte cache scrub (cold MALL "
-                   "and L2); warm: back-to-back calls" % SCRUB_BYTES),
+                   "and L2); warm: back-to-back calls; clean_cold: each call after a read "
+                   "of a 1 GiB buffer instead of the fill" % SCRUB_BYTES),
         "timed_steps": {"calls_bracketed": len(calls), "median_us": float(np.median(call_us)),
                         "p10_us": float(np.percentile(call_us, 10)),
                         "p90_us": float(np.percentile(call_us, 90)),
@@ -706,6 +752,7 @@ def main():
                         "wall_s": timed_region_s},
         "warm": warm,
         "warm_GBs": (kv_bytes / (warm["us_per_call"] * 1e-6) / 1e9) if warm else None,
+        "clean_cold": clean,
         "graph_us_per_call": graph_us,
         "graph_replay_events": graph_events,
         "append_draft": append,
