@@ -968,9 +968,9 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
 
 // Epilogue helpers.  The staging layout: row r of a wave's region is 512 bytes
 // (its 128 dims in fp32), the 16-byte granule g (dims 4g..4g+3 of the slice)
-// at slot g ^ r.  The writes go down a column (one granule of 32 rows) and the
-// reads along rows (8 lanes a row, every other granule); with the XOR both
-// spread over all banks.  A slot address is the lane's base XOR a constant:
+// at slot g ^ r.  The writes go down columns (a write: granules 2j, 2j+1 of
+// 32 rows) and the reads along rows (8 lanes a row, every other granule); with
+// the XOR both spread over all banks.  A slot address is the lane's base XOR a constant:
 // the base holds the row's 512-aligned offset and the lane's own bits of the
 // slot, the constant the granule bits the instruction picks.
 //
