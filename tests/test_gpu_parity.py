@@ -166,6 +166,26 @@ def test_small_shapes(seed, prefix, ndraft, H, ns, out_f32, flags):
     full_check(w, num_splits=ns, out_f32=out_f32, label="small%d" % seed, flags=flags)
 
 
+# Row counts around the epilogue's 32-row blocks: one workgroup holds 1, 31,
+# 33, 64, 97, 127 or 128 rows (and 129: a second workgroup of one row), so the
+# staging rounds end on a partial block, a whole one and every block count
+# from 1 to 4.  H = 1 reads the packed visibility words, H = 8 the mask bytes.
+EPILOGUE_ROWS = [(1, 1), (31, 1), (33, 1), (64, 1), (97, 1), (127, 1), (129, 1),
+                 (4, 8), (12, 8), (16, 8), (17, 8)]
+
+
+@pytest.mark.parametrize("ndraft,H", EPILOGUE_ROWS)
+@pytest.mark.parametrize("ns", [1, 2])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_epilogue_row_counts(ndraft, H, ns, flags):
+    """Every row against the oracle, fp32 output at the literal bar, with one
+    split (the output written by the split kernel) and two (partials and the
+    merge)."""
+    print("epilogue rows=%d H=%d ns=%d flags=%d" % (ndraft * H, H, ns, flags), flush=True)
+    w = W.small(300 + ndraft, [70], [ndraft], num_heads=H)
+    full_check(w, num_splits=ns, out_f32=True, label="rows%d" % (ndraft * H), flags=flags)
+
+
 def test_random_masks_many_splits():
     """Masks that are not trees (arbitrary visibility, rows with no visible key)."""
     w = W.small(220, [90, 13], [7, 4], num_heads=4)
