@@ -711,20 +711,36 @@ __device__ __forceinline__ void pv_tile(const lds_u8* sb, const SplitCtx& c, con
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       if (__any(a4[rb] != 1.f)) {
-        // element by element, in place in the AGPRs: O must never have a
-        // definition outside the accumulator register class in the loop
+        // in place in the AGPRs (O must never have a definition outside the
+        // accumulator register class in the loop), one asm block per
+        // accumulator: read, multiply and write back four elements at a time
+        // through four VGPRs.  (One block per element made the compiler pad
+        // each with a wait state: a fourth instruction per element.)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float tmp;
-            asm volatile(
-                "v_accvgpr_read_b32 %1, %0\n\t"
-                "v_mul_f32 %1, %1, %2\n\t"
-                "v_accvgpr_write_b32 %0, %1"
-                : "+a"(O[4 * db + rb][r]), "=&v"(tmp)
-                : "v"(a4[rb]));
-          }
+          f32x16& o = O[4 * db + rb];
+          float t0, t1, t2, t3;
+#define TV_RESCALE4(i0, i1, i2, i3)                 \
+  "v_accvgpr_read_b32 %16, %" #i0 "\n\t"          \
+  "v_accvgpr_read_b32 %17, %" #i1 "\n\t"          \
+  "v_accvgpr_read_b32 %18, %" #i2 "\n\t"          \
+  "v_accvgpr_read_b32 %19, %" #i3 "\n\t"          \
+  "v_mul_f32 %16, %16, %20\n\t"                   \
+  "v_mul_f32 %17, %17, %20\n\t"                   \
+  "v_mul_f32 %18, %18, %20\n\t"                   \
+  "v_mul_f32 %19, %19, %20\n\t"                   \
+  "v_accvgpr_write_b32 %" #i0 ", %16\n\t"         \
+  "v_accvgpr_write_b32 %" #i1 ", %17\n\t"         \
+  "v_accvgpr_write_b32 %" #i2 ", %18\n\t"         \
+  "v_accvgpr_write_b32 %" #i3 ", %19\n\t"
+          asm volatile(TV_RESCALE4(0, 1, 2, 3) TV_RESCALE4(4, 5, 6, 7)
+                       TV_RESCALE4(8, 9, 10, 11) TV_RESCALE4(12, 13, 14, 15)
+                       : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
+                         "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
+                         "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
+                         "+a"(o[15]), "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+                       : "v"(a4[rb]));
+#undef TV_RESCALE4
         }
       }
     }
