@@ -334,18 +334,22 @@ def test_repeat_calls_are_deterministic():
 
 @pytest.mark.parametrize("flags", [0, 1])
 def test_score_jumps_beyond_headroom_rescale(flags):
-    """Rows whose maximum jumps by far more than 2^64 (log2 units) after their
-    first tile, twice in a row (the reference moves and O and l are rescaled
-    each time), in a split that also holds rows without a jump."""
+    """Rows whose maximum jumps by far more than the headroom after their first
+    tile, twice in a row (the reference moves and O and l are rescaled each
+    time), in a split that also holds rows without a jump.  A reference sits
+    60 (log2 units) above the maximum that set it and moves on a score more
+    than 64 above it: the jumps here are ~140 and ~150 above the previous
+    maximum (log2 units).  The large components sit in RoPE dims (keys only,
+    not values), so the outputs stay of unit size."""
     w = W.small(240, [400], [4], num_heads=2)
     qv = W.bf16_to_f32(w.q).copy()
     qv[1, 0, :] = 0
-    qv[1, 0, 7] = 40.0
-    qv[2, 1, 9] = 40.0
+    qv[1, 0, 520] = 40.0
+    qv[2, 1, 530] = 40.0
     w.q[:] = W.bf16_round(qv)
-    for key, dim, val in ((170, 7, 20.0), (300, 7, 40.0), (250, 9, 40.0)):
+    for key, dim, val in ((170, 520, 36.0), (300, 520, 72.0), (250, 530, 72.0)):
         k = W.bf16_to_f32(w.kv[w.kv_indices[key]]).copy()
-        k[dim] = val  # score jumps of 0.072 * 800 = 58 and 0.072 * 1600 = 115 natural units
+        k[dim] = val  # scores of 0.072 * 1440 = 104 and 0.072 * 2880 = 208 natural units
         w.kv[w.kv_indices[key]] = W.bf16_round(k)
     for ns in (1, 3):
         print("jump ns=%d flags=%d" % (ns, flags), flush=True)
