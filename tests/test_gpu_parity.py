@@ -114,6 +114,16 @@ def test_c5_large_batch_with_outliers(out_f32):
     print("   %s" % st, flush=True)
 
 
+def test_c5_precise_every_row():
+    """Every row of the x30-outlier batch in precise mode, fp32 output, at the
+    bar: outlier x outlier scores move references by hundreds (log2 units)
+    in about a fifth of the tiles, and a row that loses earlier terms at a move
+    shows here even when a sample of rows misses it."""
+    print("C5 precise, every row", flush=True)
+    st = full_check(W.config(5), out_f32=True, label="C5 precise all rows", flags=PRECISE)
+    print("   %s" % st, flush=True)
+
+
 @pytest.mark.parametrize("out_f32", [False, True])
 def test_c5_default_mode_stays_within_its_derived_error_bound(out_f32):
     """NOT a parity-bar test: without the precise flag the x30 outliers put the
@@ -334,13 +344,12 @@ def test_repeat_calls_are_deterministic():
 
 @pytest.mark.parametrize("flags", [0, 1])
 def test_score_jumps_beyond_headroom_rescale(flags):
-    """Rows whose maximum jumps by far more than the headroom after their first
-    tile, twice in a row (the reference moves and O and l are rescaled each
-    time), in a split that also holds rows without a jump.  A reference sits
-    60 (log2 units) above the maximum that set it and moves on a score more
-    than 64 above it: the jumps here are ~140 and ~150 above the previous
-    maximum (log2 units).  The large components sit in RoPE dims (keys only,
-    not values), so the outputs stay of unit size."""
+    """Rows whose maximum jumps by far more than 2^64 (log2 units) after their
+    first tile, twice in a row (the reference moves and O and l are rescaled
+    each time), in a split that also holds rows without a jump: scores of
+    ~150 and ~300 (log2 units) after a first tile of unit scores.  The large
+    components sit in RoPE dims (keys only, not values), so the outputs stay
+    of unit size."""
     w = W.small(240, [400], [4], num_heads=2)
     qv = W.bf16_to_f32(w.q).copy()
     qv[1, 0, :] = 0
@@ -354,6 +363,60 @@ def test_score_jumps_beyond_headroom_rescale(flags):
     for ns in (1, 3):
         print("jump ns=%d flags=%d" % (ns, flags), flush=True)
         full_check(w, num_splits=ns, out_f32=True, label="jump ns=%d" % ns, flags=flags)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_score_jumps_in_value_dims(flags):
+    """The same two-jump pattern with the large components in value dims (the
+    outputs then hold values up to 40): scores of 58 and 115 natural units
+    after a first tile of unit scores."""
+    w = W.small(240, [400], [4], num_heads=2)
+    qv = W.bf16_to_f32(w.q).copy()
+    qv[1, 0, :] = 0
+    qv[1, 0, 7] = 40.0
+    qv[2, 1, 9] = 40.0
+    w.q[:] = W.bf16_round(qv)
+    for key, dim, val in ((170, 7, 20.0), (300, 7, 40.0), (250, 9, 40.0)):
+        k = W.bf16_to_f32(w.kv[w.kv_indices[key]]).copy()
+        k[dim] = val  # scores of 0.072 * 800 = 58 and 0.072 * 1600 = 115 natural units
+        w.kv[w.kv_indices[key]] = W.bf16_round(k)
+    for ns in (1, 3):
+        print("jump (value dims) ns=%d flags=%d" % (ns, flags), flush=True)
+        full_check(w, num_splits=ns, out_f32=True, label="jump v ns=%d" % ns, flags=flags)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_move_just_past_the_threshold_keeps_the_earlier_terms(flags):
+    """After a first tile of zero scores a row meets a key scoring ~123.4
+    (log2 units) and then one scoring ~126.5: the first holds about an eighth
+    of the row's mass.  Whatever references and moves the kernel uses, no
+    factor 2^(old - new) may flush it (a reference placed 60 above the first
+    maximum would not move at the first key and would need 2^-126.5, below
+    the smallest normal fp32, at the second)."""
+    w = W.small(241, [300], [4], num_heads=2)
+    qv = W.bf16_to_f32(w.q).copy()
+    qv[1, 0, :] = 0
+    qv[1, 0, 520] = 40.0
+    w.q[:] = W.bf16_round(qv)
+    kv = W.bf16_to_f32(w.kv).copy()
+    kv[w.kv_indices, 520] = 0.0  # every other key of the row scores exactly 0
+    kv[w.kv_indices[40], 520] = 29.625  # tile 1
+    kv[w.kv_indices[100], 520] = 30.375  # tile 3
+    w.kv[:] = W.bf16_round(kv)
+    s2 = float(w.sm_scale) * 1.4426950408889634 * 40.0
+    s_old, s_new = s2 * 29.625, s2 * 30.375
+    # the pattern: the second key ~3.1 above the first, both ~124 above the rest
+    assert 123.0 < s_old < 124.0 and 3.0 < s_new - s_old < 3.3
+    # precise mode at the bar; the default mode within its derived bounds (per
+    # element and relative): two keys carry nearly all the mass, so the bf16
+    # rounding of their probabilities does not average out (flushing the
+    # first key would miss by ~0.46, ~12 % relative)
+    bounds = {} if flags else {"extra_abs": p_rounding_bound(w, precise=False),
+                                 "mean_rel_max": 2.0 ** -8 + 2.0 ** -11}
+    for ns in (1, 3):
+        print("move past the threshold ns=%d flags=%d" % (ns, flags), flush=True)
+        full_check(w, num_splits=ns, out_f32=True, label="move ns=%d" % ns, flags=flags,
+                   **bounds)
 
 
 @pytest.mark.parametrize("e", [20, -20])

@@ -42,14 +42,12 @@
 //    the softmax of tile t+1, a few fenced instructions after each MFMA (one
 //    wave per SIMD issues about one instruction every four cycles, so only a
 //    handful fit beside each MFMA for free).
-//  * Reference maximum with thresholded rescaling: a row's reference is set
-//    REF_LIFT above the maximum of its first tile with a visible key (O and l
-//    are still exactly 0 then) and moves only when a score exceeds it by more
-//    than TAU (log2 units), again to REF_LIFT above that tile's maximum.
-//    Probabilities exp2(x - ref) lie below 2^-REF_LIFT at first and may grow
-//    to 2^TAU, which fp32 sums and bf16 operands hold at full relative
-//    precision, so in the common case no VALU work touches the accumulators;
-//    the lift lets a row's maximum climb TAU + REF_LIFT before it moves.  When a row's reference moves, its l and O are scaled by
+//  * Reference maximum with thresholded rescaling: a row's reference is set at
+//    the maximum of its first tile with a visible key (O and l are still
+//    exactly 0 then) and moves only when a score exceeds it by more than TAU
+//    (log2 units).  Probabilities exp2(x - ref) may grow to 2^TAU, which fp32
+//    sums and bf16 operands hold, so in the common case no VALU work touches
+//    the accumulators.  When a row's reference moves, its l and O are scaled by
 //    2^(old - new): the factors go through LDS (every wave holds a slice of
 //    every row's O), and each wave rescales, in place in the AGPRs, only the
 //    32-row blocks that hold a moved row.
@@ -75,7 +73,6 @@ constexpr int NSTAGE = 3;
 constexpr int DMA_PER_TILE = 10;          // direct-to-LDS loads per wave per tile
 constexpr int SLOT_RING = 4;              // tiles of gather slots held per wave in LDS
 constexpr float TAU = 64.0f;              // log2 headroom of a probability over its reference
-constexpr float REF_LIFT = 60.0f;         // a reference sits this far (log2) above the maximum setting it
 
 // A key's 1024 latent bytes sit at key*ROW + key_shift(key).  Modulo 256 bytes
 // (one pass over the banks) that is 64*(key & 3) + 16*((key >> 2) & 3): the 16
@@ -557,23 +554,20 @@ __device__ __forceinline__ void soft_step(int step, Soft& sm, f32x16& S, MaskSel
     sm.tmax = max3f(m, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
     fence(sm.tmax);
   } else if (step == 4) {
-    // first visible keys set the reference (O and l are still 0), REF_LIFT
-    // above their maximum, as a move does below
+    // first visible keys set the reference (O and l are still 0)
     fence(sm.tmax);
-    const float lifted = sm.tmax + REF_LIFT;
-    sm.ref0 = (m_ref == -INFINITY) ? lifted : m_ref;
-    sm.alpha_j = __builtin_amdgcn_exp2f(sm.ref0 - lifted);
+    sm.ref0 = (m_ref == -INFINITY) ? sm.tmax : m_ref;
+    sm.alpha_j = __builtin_amdgcn_exp2f(sm.ref0 - sm.tmax);
     fence(sm.ref0);
     fence(sm.alpha_j);
   } else if (step == 5) {
-    // a score more than TAU above the reference moves it to REF_LIFT above
-    // the tile's maximum, and l and O are scaled by 2^(old - new) (alpha is
-    // exactly 1 otherwise)
+    // a score more than TAU above the reference moves it, and l and O are
+    // scaled by 2^(old - new) (alpha is exactly 1 otherwise)
     fence(sm.alpha_j);
     const bool jump = sm.tmax > sm.ref0 + TAU;
     const float alpha = jump ? sm.alpha_j : 1.f;
     l_sum *= alpha;
-    m_ref = jump ? sm.tmax + REF_LIFT : sm.ref0;
+    m_ref = jump ? sm.tmax : sm.ref0;
     sm.alpha_j = alpha;
     fence(sm.alpha_j);
     fence(l_sum);
@@ -1225,19 +1219,9 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
                  "+a"(O[12]), "+a"(O[13]), "+a"(O[14]), "+a"(O[15]));
   const float l_tot = l_sum + __shfl_xor(l_sum, 32);
   const bool empty = !(l_tot > 0.f);
-  // lse = ref + log2 l (then in natural units).  ref sits REF_LIFT above a
-  // maximum and l about 2^-REF_LIFT below its size, so ref + log2 l in one
-  // sum would cancel two numbers of magnitude ~60 (fp32 ulp ~4e-6); instead,
-  // with l = m * 2^e: (ref - REF_LIFT) (exact for ref >= REF_LIFT / 2, the
-  // same size as the maximum otherwise) + (e + REF_LIFT) (an exact integer)
-  // + log2 m (|log2 m| <= 1).  v_log_f32 is log2.
-  const int l_exp = __builtin_amdgcn_frexp_expf(l_tot);
-  const float l_mant = __builtin_amdgcn_frexp_mantf(l_tot);
-  const float lse_nat =
-      empty ? -INFINITY
-            : (((m_ref - REF_LIFT) + (float)(l_exp + (int)REF_LIFT)) +
-               __builtin_amdgcn_logf(l_mant)) *
-                  0.69314718055994530942f;
+  // v_log_f32 is log2
+  const float lse_nat = empty ? -INFINITY
+                              : (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
   if (half == 0) inv_s[wave * 32 + l32] = empty ? 0.f : 1.f / l_tot;
   if (c.row_ok && half == 0) {
     if (nsplit == 1) lse_[g] = lse_nat;
