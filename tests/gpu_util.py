@@ -22,10 +22,27 @@ def p_rounding_bound(w: W.Workload, precise: bool):
     fp16 (11 significant bits) under an exact power-of-two scale: each is a convex
     combination of value rows, so that adds at most 2^-11 max_j |v_jd| (fp32
     partials in precise mode add nothing at this scale)."""
-    v = W.bf16_to_f32(w.kv[np.unique(w.kv_indices)][:, :512]) if w.kv_indices.size else \
-        np.zeros((1, 512), np.float32)
+    slots = referenced_slots(w)
+    v = W.bf16_to_f32(w.kv[slots][:, :512]) if slots.size else np.zeros((1, 512), np.float32)
     u = 2.0 ** -16 if precise else 2.0 ** -8 + 2.0 ** -11
     return u * np.abs(v).max(axis=0).astype(np.float64)
+
+
+def referenced_slots(w: W.Workload) -> np.ndarray:
+    """The pool rows the requests read: every kv_indices entry, or in the
+    contiguous-prefix form each prefix as the run from its first slot (its
+    other prefix entries are placeholders) followed by the draft slots."""
+    if not w.contiguous_prefix:
+        return np.unique(w.kv_indices)
+    out = []
+    for b in range(w.batch):
+        k0 = int(w.kv_indptr[b])
+        L, n = int(w.kv_lens[b]), int(w.q_lens[b])
+        P = L - n
+        if P > 0:
+            out.append(int(w.kv_indices[k0]) + np.arange(P, dtype=np.int64))
+        out.append(w.kv_indices[k0 + P:k0 + L].astype(np.int64))
+    return np.unique(np.concatenate(out)) if out else np.zeros(0, np.int64)
 
 
 def torch_mod():
