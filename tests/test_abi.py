@@ -115,6 +115,22 @@ def test_plan_heuristic_fills_the_chip():
     assert tv.workspace_bytes(p) >= 32 * pl["max_splits"] * 12 * 4
 
 
+def test_plan_of_a_batch_of_equal_requests():
+    """8 requests of one token x 128 heads, every one at the 32769-key maximum
+    (the key list holds exactly 8 x 32769 entries): one workgroup per compute
+    unit, as for a single request, and no dispatch order; one entry fewer and
+    the batch counts as unequal, about two per unit."""
+    base = dict(batch=8, num_heads=128, total_q=8, max_q_len=1, max_kv_len=32769,
+                total_mask=8 * 32769, num_slots=262144)
+    pl = tv.plan(prob(total_kv=8 * 32769, **base))
+    assert pl["row_blocks"] == 1 and 240 <= 8 * pl["max_splits"] <= 256
+    prow = 8 * 128 * pl["max_splits"]
+    align = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert pl["workspace_bytes"] == align(prow * 1024) + align(prow * 8)  # no order
+    pl2 = tv.plan(prob(total_kv=8 * 32769 - 1, **base))
+    assert 8 * pl2["max_splits"] > 256
+
+
 def test_no_dispatch_order_when_every_work_item_has_a_compute_unit():
     """8 requests of 128 rows, keys up to 3968: at most 256 work items, all
     resident at once, so no longest-first order (and no pack launch)."""

@@ -102,9 +102,13 @@ tv_status make_layout(const tv_problem* p, Layout* lay) {
   } else {
     // splits of >= 4 tiles; one workgroup per compute unit over the whole
     // request, or for a batch (requests of unequal lengths, dispatched longest
-    // first) about two, so that the schedule has pieces to balance with
+    // first) about two, so that the schedule has pieces to balance with.  A
+    // key list of exactly batch * max_kv_len entries holds every request at
+    // max_kv_len: nothing to balance, and a second workgroup per unit would
+    // only pay the per-workgroup start and end twice
     const int64_t kv_tiles = ceil_div(std::max<int64_t>(p->total_kv, L), tv::TILE_KEYS);
-    const int64_t share = p->batch > 1 ? 2 * kCUs : kCUs;
+    const bool uniform = p->total_kv == (int64_t)p->batch * L;
+    const int64_t share = p->batch > 1 && !uniform ? 2 * kCUs : kCUs;
     const int64_t per_wg =
         std::max<int64_t>(kMinSplitTiles, ceil_div(row_blocks * kv_tiles, share));
     split_keys = std::min<int64_t>(per_wg, ceil_div(L, tv::TILE_KEYS)) * tv::TILE_KEYS;
