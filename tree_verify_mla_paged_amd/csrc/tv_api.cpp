@@ -244,6 +244,13 @@ tv_status verify(const tv_problem* p, const void* q, const void* kv_buf,
   sp.wide = p->num_slots * (int64_t)(TV_QK_DIM * 2) > (int64_t)UINT32_MAX;
   sp.precise = (p->flags & TV_FLAG_PRECISE_P) != 0;
   sp.contig = (p->flags & TV_FLAG_CONTIGUOUS_PREFIX) != 0;
+  // one row block: no workgroup shares a gathered tile with another, and the
+  // streaming hint keeps the rows from displacing (and writing back) what the
+  // caches hold.  Measured cold, one box: S3 call 113 -> 75 us, D 139 -> 98,
+  // S1 37.7 -> 30.7; clean-cold unchanged; warm S1 and S3 +8-9 % (the next
+  // call no longer finds the rows in the memory-side cache).  With several
+  // row blocks (C3) cold gained ~1 % and warm lost 9 %: left off there.
+  sp.stream_kv = lay.plan.row_blocks == 1;
   const int grid = (int)lay.grid;
   if (tv::launch_split(sp, grid, s, ev0, ev1) != hipSuccess) return TV_ERR_LAUNCH;
 

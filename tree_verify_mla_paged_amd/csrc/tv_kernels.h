@@ -85,6 +85,9 @@ struct SplitParams {
   // contiguous-prefix form: prefix key j of request b is pool slot
   // kv_indices[kv_indptr[b]] + j; the other prefix entries are not read
   bool contig;
+  // key rows loaded non-temporal: set for plans of one row block, where each
+  // gathered tile is read by one workgroup only
+  bool stream_kv;
 };
 
 struct MergeParams {

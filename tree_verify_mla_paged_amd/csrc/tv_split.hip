@@ -72,6 +72,8 @@ constexpr int STAGE = MAIN_BYTES + ROPE_BYTES + MASKW_BYTES;  // 39936
 constexpr int NSTAGE = 3;
 constexpr int DMA_PER_TILE = 10;          // direct-to-LDS loads per wave per tile
 constexpr int SLOT_RING = 4;              // tiles of gather slots held per wave in LDS
+constexpr int GM_WIDE = 1;  // gather modes: 64-bit gather addresses
+constexpr int GM_NT = 2;    // non-temporal key row loads
 constexpr float TAU = 64.0f;              // log2 headroom of a probability over its reference
 
 // A key's 1024 latent bytes sit at key*ROW + key_shift(key).  Modulo 256 bytes
@@ -148,11 +150,25 @@ struct SplitCtx {
 // address is an SGPR base plus a 32-bit VGPR offset, or a 64-bit VGPR address.
 // The instruction between the M0 write and the load is the one wait state that
 // write needs.
+// NT: the key rows are loaded non-temporal (a streaming hint): plans whose
+// tiles are read by one workgroup each (one row block) take them once per call,
+// and the hint keeps them from displacing what the caches already hold, dirty
+// lines included, whose write-back would otherwise share the call's memory
+// bandwidth.  Plans of several row blocks leave it off: their row blocks read
+// each tile in turn from the L2, and back-to-back calls reuse the
+// memory-side cache.
+template <bool NT>
 __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(vaddr), "s"(m0)
-               : "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(vaddr), "s"(m0)
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(vaddr), "s"(m0)
+                 : "m0");
 }
 __device__ __forceinline__ void dma4_s(uint32_t voff, const void* sbase, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
@@ -160,36 +176,62 @@ __device__ __forceinline__ void dma4_s(uint32_t voff, const void* sbase, uint32_
                : "v"(voff), "s"(sbase), "s"(m0)
                : "m0");
 }
+template <bool NT>
 __device__ __forceinline__ void dma16_m0(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(m0)
-               : "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "m0");
 }
 // Pool row gathers of a pool under 4 GiB in three instructions: M0 = stage
 // target + OFF, byte offset = slot * 1152 + lane chunk (v_mad_u32_u24: slots
 // stay below 2^24 there), 16 bytes per lane.  The slot is wave-uniform (SGPR,
 // a key's latent row) or per lane (VGPR, the RoPE chunks of 8 keys).
-template <int OFF>
+template <int OFF, bool NT>
 __device__ __forceinline__ void dma_row_s(uint32_t mb, int slot, const SplitCtx& c) {
   uint32_t a;
-  asm volatile(
-      "s_add_u32 m0, %1, %2\n\t"
-      "v_mad_u32_u24 %0, %3, %4, %5\n\t"
-      "global_load_lds_dwordx4 %0, %6"
-      : "=&v"(a)
-      : "s"(mb), "n"(OFF), "s"(slot), "v"(c.rowb), "v"(c.voff), "s"(c.kv)
-      : "m0", "scc");
+  if constexpr (NT)
+    asm volatile(
+        "s_add_u32 m0, %1, %2\n\t"
+        "v_mad_u32_u24 %0, %3, %4, %5\n\t"
+        "global_load_lds_dwordx4 %0, %6 nt"
+        : "=&v"(a)
+        : "s"(mb), "n"(OFF), "s"(slot), "v"(c.rowb), "v"(c.voff), "s"(c.kv)
+        : "m0", "scc");
+  else
+    asm volatile(
+        "s_add_u32 m0, %1, %2\n\t"
+        "v_mad_u32_u24 %0, %3, %4, %5\n\t"
+        "global_load_lds_dwordx4 %0, %6"
+        : "=&v"(a)
+        : "s"(mb), "n"(OFF), "s"(slot), "v"(c.rowb), "v"(c.voff), "s"(c.kv)
+        : "m0", "scc");
 }
+template <bool NT>
 __device__ __forceinline__ void dma_row_v(uint32_t mb, int slot, uint32_t vo, const SplitCtx& c) {
   uint32_t a;
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "v_mad_u32_u24 %0, %2, %3, %4\n\t"
-      "global_load_lds_dwordx4 %0, %5"
-      : "=&v"(a)
-      : "s"(mb), "v"(slot), "v"(c.rowb), "v"(vo), "s"(c.kv)
-      : "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_mad_u32_u24 %0, %2, %3, %4\n\t"
+        "global_load_lds_dwordx4 %0, %5 nt"
+        : "=&v"(a)
+        : "s"(mb), "v"(slot), "v"(c.rowb), "v"(vo), "s"(c.kv)
+        : "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "v_mad_u32_u24 %0, %2, %3, %4\n\t"
+        "global_load_lds_dwordx4 %0, %5"
+        : "=&v"(a)
+        : "s"(mb), "v"(slot), "v"(c.rowb), "v"(vo), "s"(c.kv)
+        : "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
@@ -276,43 +318,45 @@ __device__ __forceinline__ GatherDst gather_dst(const lds_u8* sb, const SplitCtx
 //   piece 8:    RoPE dims of the wave's 8 keys (one slot per 8 lanes);
 //   piece 9:    the visibility words of the tile (one per draft row), unless
 //               the mask bytes are read directly (mask_load).
-// WIDE: the pool may exceed 4 GiB, so the gathers use 64-bit addresses.  The
-// slots are taken by reference to the caller's array (a pointer kept in a
-// struct makes the compiler move the array to memory).
-template <bool WIDE, int J>
+// GM, the gather mode: bit 0 (GM_WIDE) the pool may exceed 4 GiB, so the
+// gathers use 64-bit addresses; bit 1 (GM_NT) the key rows are non-temporal
+// loads (dma16_v).  The slots are taken by reference to the caller's array (a
+// pointer kept in a struct makes the compiler move the array to memory).
+template <int GM, int J>
 __device__ __forceinline__ void gather_piece(const GatherDst& g, const int (&slot)[8], int slane,
                                              const SplitCtx& c, int t) {
+  constexpr bool WIDE = (GM & GM_WIDE) != 0, NT = (GM & GM_NT) != 0;
   if constexpr (J < 8) {
     constexpr int OFF = J * ROW + 16 * (J >> 2);
-    if constexpr (WIDE) dma16_m0(c.voff, c.kv + (int64_t)slot[J] * QK, g.main + OFF);
-    else dma_row_s<OFF>(g.main, slot[J], c);
+    if constexpr (WIDE) dma16_m0<NT>(c.voff, c.kv + (int64_t)slot[J] * QK, g.main + OFF);
+    else dma_row_s<OFF, NT>(g.main, slot[J], c);
   } else if constexpr (J == 8) {
     if constexpr (WIDE) {
-      dma16_v(reinterpret_cast<const uint8_t*>(c.kv) + (int64_t)slane * (QK * 2) + c.rp_voff,
-              g.rope);
+      dma16_v<NT>(reinterpret_cast<const uint8_t*>(c.kv) + (int64_t)slane * (QK * 2) + c.rp_voff,
+                  g.rope);
     } else {
-      dma_row_v(g.rope, slane, c.rp_voff, c);
+      dma_row_v<NT>(g.rope, slane, c.rp_voff, c);
     }
   } else {
     if (!c.mbytes) dma4_s(c.wvoff, c.wbase + min(t, c.ntiles - 1), g.mask);
   }
 }
 
-template <bool WIDE>
+template <int GM>
 __device__ __forceinline__ void issue_tile(const lds_u8* sb, const int (&slot)[8], int slane,
                                            const SplitCtx& c, int t) {
   static_assert(DMA_PER_TILE == 10, "");
   const GatherDst g = gather_dst(sb, c);
-  gather_piece<WIDE, 0>(g, slot, slane, c, t);
-  gather_piece<WIDE, 1>(g, slot, slane, c, t);
-  gather_piece<WIDE, 2>(g, slot, slane, c, t);
-  gather_piece<WIDE, 3>(g, slot, slane, c, t);
-  gather_piece<WIDE, 4>(g, slot, slane, c, t);
-  gather_piece<WIDE, 5>(g, slot, slane, c, t);
-  gather_piece<WIDE, 6>(g, slot, slane, c, t);
-  gather_piece<WIDE, 7>(g, slot, slane, c, t);
-  gather_piece<WIDE, 8>(g, slot, slane, c, t);
-  gather_piece<WIDE, 9>(g, slot, slane, c, t);
+  gather_piece<GM, 0>(g, slot, slane, c, t);
+  gather_piece<GM, 1>(g, slot, slane, c, t);
+  gather_piece<GM, 2>(g, slot, slane, c, t);
+  gather_piece<GM, 3>(g, slot, slane, c, t);
+  gather_piece<GM, 4>(g, slot, slane, c, t);
+  gather_piece<GM, 5>(g, slot, slane, c, t);
+  gather_piece<GM, 6>(g, slot, slane, c, t);
+  gather_piece<GM, 7>(g, slot, slane, c, t);
+  gather_piece<GM, 8>(g, slot, slane, c, t);
+  gather_piece<GM, 9>(g, slot, slane, c, t);
 }
 
 // The MFMAs of the tile loop are inline asm: S^T accumulates in VGPRs and O^T
@@ -651,21 +695,21 @@ __device__ __forceinline__ void write_p(lds_u8* pb, const SplitCtx& c, const Sof
 }
 
 // gather_piece with the piece number known only after unrolling
-template <bool WIDE>
+template <int GM>
 __device__ __forceinline__ void gather_piece_n(int j, const GatherDst& g, const int (&slot)[8],
                                                int slane, const SplitCtx& c, int t) {
   static_assert(DMA_PER_TILE == 10, "");
   switch (j) {
-    case 0: gather_piece<WIDE, 0>(g, slot, slane, c, t); break;
-    case 1: gather_piece<WIDE, 1>(g, slot, slane, c, t); break;
-    case 2: gather_piece<WIDE, 2>(g, slot, slane, c, t); break;
-    case 3: gather_piece<WIDE, 3>(g, slot, slane, c, t); break;
-    case 4: gather_piece<WIDE, 4>(g, slot, slane, c, t); break;
-    case 5: gather_piece<WIDE, 5>(g, slot, slane, c, t); break;
-    case 6: gather_piece<WIDE, 6>(g, slot, slane, c, t); break;
-    case 7: gather_piece<WIDE, 7>(g, slot, slane, c, t); break;
-    case 8: gather_piece<WIDE, 8>(g, slot, slane, c, t); break;
-    default: gather_piece<WIDE, 9>(g, slot, slane, c, t); break;
+    case 0: gather_piece<GM, 0>(g, slot, slane, c, t); break;
+    case 1: gather_piece<GM, 1>(g, slot, slane, c, t); break;
+    case 2: gather_piece<GM, 2>(g, slot, slane, c, t); break;
+    case 3: gather_piece<GM, 3>(g, slot, slane, c, t); break;
+    case 4: gather_piece<GM, 4>(g, slot, slane, c, t); break;
+    case 5: gather_piece<GM, 5>(g, slot, slane, c, t); break;
+    case 6: gather_piece<GM, 6>(g, slot, slane, c, t); break;
+    case 7: gather_piece<GM, 7>(g, slot, slane, c, t); break;
+    case 8: gather_piece<GM, 8>(g, slot, slane, c, t); break;
+    default: gather_piece<GM, 9>(g, slot, slane, c, t); break;
   }
 }
 
@@ -815,7 +859,7 @@ __device__ __forceinline__ void split_slots(const SplitCtx& c) {
 }
 // split_gathers: once the slots have landed (the caller waits), the gathers of
 // tiles 0 and 1 and their mask bytes.
-template <bool WIDE>
+template <int GM>
 __device__ __forceinline__ void split_gathers(lds_u8* stages, const SplitCtx& c, MaskBytes& m0,
                                               MaskBytes& m1) {
   int slot[8];
@@ -827,12 +871,12 @@ __device__ __forceinline__ void split_gathers(lds_u8* stages, const SplitCtx& c,
     mask_load(m0, c, 0);
     mask_load(m1, c, 1);  // (past the split: real bytes or zeros, unused)
   }
-  issue_tile<WIDE>(stages, slot, r.slane, c, 0);
+  issue_tile<GM>(stages, slot, r.slane, c, 0);
   if (c.ntiles > 1) {
     slot_load(r, c, 1);
     slot_take(slot, r, 0);
     slot_take(slot, r, 1);
-    issue_tile<WIDE>(stages + STAGE, slot, r.slane, c, 1);
+    issue_tile<GM>(stages + STAGE, slot, r.slane, c, 1);
   }
 }
 
@@ -855,7 +899,7 @@ __device__ __forceinline__ int alpha_moved(float a0, float a1) {
 // holds tile t+1's, turned into the word early in the chain, and then receives
 // tile t+2's); the softmax's first step picks one (MaskSel), so that nothing
 // in the chain waits for the word's LDS read.
-template <bool WIDE, bool PRECISE, bool GATHER, bool CONTIG>
+template <int GM, bool PRECISE, bool GATHER, bool CONTIG>
 __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
                                            const bf16x8 (&qf)[QK / 16], const float* alpha_t,
                                            int t, int cur, int nx1, int nx2, uint32_t& mww,
@@ -886,7 +930,7 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
       fence(a1);
       resc = alpha_moved(a0, a1);
     } else if (ks >= G0 && ks < G0 + 3 * DMA_PER_TILE && (ks - G0) % 3 == 0) {
-      if (GATHER) gather_piece_n<WIDE>((ks - G0) / 3, g, slot, r.slane, c, t + 2);
+      if (GATHER) gather_piece_n<GM>((ks - G0) / 3, g, slot, r.slane, c, t + 2);
       if (GATHER && ks == G0 + 3 * (DMA_PER_TILE - 1) && c.mbytes) mask_load(mb, c, t + 2);
     } else if (ks == G0 + 3 * DMA_PER_TILE - 2) {
       if (!c.mbytes) mww = tile_word(stages + nx1 * STAGE, c);
@@ -907,7 +951,7 @@ __device__ __forceinline__ f32x16 qk_phase(lds_u8* stages, const SplitCtx& c,
 // iteration issues nothing else to global memory), P(t) and tile t's factors,
 // and frees stage t-1, P buffer t-1 and factors t-1 for reuse.  The softmax of
 // tile 0 runs ahead of the loop.
-template <bool WIDE, bool PRECISE, bool CONTIG>
+template <int GM, bool PRECISE, bool CONTIG>
 __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds_u8* pbuf,
                                           bf16x8 (&qf)[QK / 16], f32x16 (&O)[16],
                                           float& m_ref, float& l_sum, float* alpha_s,
@@ -952,11 +996,11 @@ __device__ __forceinline__ void run_split(lds_u8* stages, const SplitCtx& c, lds
     int resc;         // some row's reference moved in tile t
     bf16x8 A0[2];
     if (t + 2 < nt) {
-      S = qk_phase<WIDE, PRECISE, true, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
+      S = qk_phase<GM, PRECISE, true, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
                                                 ms.wb, resc, A0, mb);
       ms.valid = tile_valid(c, t + 1);
     } else if (t + 1 < nt) {
-      S = qk_phase<WIDE, PRECISE, false, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
+      S = qk_phase<GM, PRECISE, false, CONTIG>(stages, c, qf, alpha_t, t, cur, nx1, nx2, ms.ww,
                                                  ms.wb, resc, A0, mb);
       ms.valid = tile_valid(c, t + 1);
     } else {
@@ -1056,7 +1100,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&O)[16]) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(O[i]) : "v"(z));
 }
 
-template <bool WIDE, bool PRECISE, bool MASKB, bool CONTIG>
+template <int GM, bool PRECISE, bool MASKB, bool CONTIG>
 __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     const uint16_t* __restrict__ q_, const uint16_t* __restrict__ kv_,
     const int32_t* __restrict__ kv_indices_, const int32_t* __restrict__ kv_indptr_,
@@ -1200,7 +1244,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
     // the slots have landed once at most the query loads are outstanding
     if (wave_q) wait_vmcnt<QK / 16>();
     else wait_vmcnt<0>();
-    split_gathers<WIDE>(stages, c, m0, mb);
+    split_gathers<GM>(stages, c, m0, mb);
   }
 
   // O^T of dims 128*wave + 32*db .. +31 (register r of lane l: dim + 8*(r/4) +
@@ -1210,7 +1254,7 @@ __global__ __launch_bounds__(256, 1) void tv_split_kernel(
   float m_ref = -INFINITY;  // reference maximum (log2 units)
   float l_sum = 0.f;        // this half's share of the normaliser
   if (c.ntiles > 0)
-    run_split<WIDE, PRECISE, CONTIG>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s, m0, mb);
+    run_split<GM, PRECISE, CONTIG>(stages, c, pbuf, qf, O, m_ref, l_sum, alpha_s, m0, mb);
 
   // the last PV MFMAs must finish before O is read out of the AGPRs
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -1342,17 +1386,19 @@ hipError_t launch_split(const SplitParams& p, int grid, hipStream_t st, hipEvent
   float* wl = p.ws_lse;
   SplitScalars sc = p.s;
   void* args[] = {&q, &kv, &kvi, &kvp, &qop, &mk, &mkp, &mw, &ord, &o, &l, &wo, &wl, &sc};
-  // [wide][precise][mask bytes][contiguous prefix]
-#define TV_SPLIT_FN(W, P, M, C) reinterpret_cast<const void*>(&tv_split_kernel<W, P, M, C>)
-#define TV_SPLIT_FN2(W, P, M) {TV_SPLIT_FN(W, P, M, false), TV_SPLIT_FN(W, P, M, true)}
-#define TV_SPLIT_FN4(W, P) {TV_SPLIT_FN2(W, P, false), TV_SPLIT_FN2(W, P, true)}
-  static const void* const fns[2][2][2][2] = {
-      {TV_SPLIT_FN4(false, false), TV_SPLIT_FN4(false, true)},
-      {TV_SPLIT_FN4(true, false), TV_SPLIT_FN4(true, true)}};
+  // [gather mode: wide | non-temporal][precise][mask bytes][contiguous prefix]
+#define TV_SPLIT_FN(G, P, M, C) reinterpret_cast<const void*>(&tv_split_kernel<G, P, M, C>)
+#define TV_SPLIT_FN2(G, P, M) {TV_SPLIT_FN(G, P, M, false), TV_SPLIT_FN(G, P, M, true)}
+#define TV_SPLIT_FN4(G, P) {TV_SPLIT_FN2(G, P, false), TV_SPLIT_FN2(G, P, true)}
+#define TV_SPLIT_FN8(G) {TV_SPLIT_FN4(G, false), TV_SPLIT_FN4(G, true)}
+  static const void* const fns[4][2][2][2] = {TV_SPLIT_FN8(0), TV_SPLIT_FN8(1), TV_SPLIT_FN8(2),
+                                              TV_SPLIT_FN8(3)};
+#undef TV_SPLIT_FN8
 #undef TV_SPLIT_FN4
 #undef TV_SPLIT_FN2
 #undef TV_SPLIT_FN
-  const void* fn = fns[p.wide][p.precise][p.s.mask_bytes != 0][p.contig];
+  const int gm = (p.wide ? GM_WIDE : 0) | (p.stream_kv ? GM_NT : 0);
+  const void* fn = fns[gm][p.precise][p.s.mask_bytes != 0][p.contig];
   if (ev0 || ev1) return hipExtLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st, ev0, ev1, 0);
   return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, st);
 }
