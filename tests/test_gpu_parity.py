@@ -1048,3 +1048,43 @@ def test_random_workloads_every_row(seed):
             kw["mean_rel_max"] = 2.0 ** -8 + 2.0 ** -11
     full_check(w, num_splits=ns, out_f32=out_f32, label="random %d" % seed,
                flags=PRECISE if precise else 0, **kw)
+
+
+def random_medium_case(seed):
+    """A workload of several row blocks and many or long splits, drawn like
+    random_case (capped at ~40M (row, key) pairs)."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 5))
+    H = int(rng.choice([8, 16, 32, 64, 128]))
+    ndr = [int(rng.integers(8, 65)) for _ in range(B)]
+    pre = [int(rng.integers(0, 20001)) for _ in range(B)]
+    while sum(n * H * (p + n) for n, p in zip(ndr, pre)) > 40_000_000:
+        pre = [p // 2 for p in pre]
+    form = str(rng.choice(["full", "full", "prefix_visible", "contiguous"]))
+    outliers = bool(rng.random() < 0.3)
+    ns = int(rng.choice([0, 0, 5, 40]))
+    out_f32 = bool(rng.random() < 0.5)
+    precise = bool(rng.random() < 0.4)
+    w = W.small(7000 + seed, pre, ndr, num_heads=H, outlier_p=0.01 if outliers else 0.0,
+                placement="contiguous" if form == "contiguous" else "random")
+    if form == "prefix_visible":
+        w = W.prefix_visible_form(w)
+    elif form == "contiguous":
+        w = W.contiguous_prefix_form(w)
+    return w, ns, out_f32, precise, outliers, "B=%d H=%d drafts=%s prefixes=%s %s ns=%d f32=%s " \
+        "precise=%s outliers=%s" % (B, H, ndr, pre, form, ns, out_f32, precise, outliers)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_medium_workloads_every_row(seed):
+    """Every row of each drawn workload of several row blocks against the
+    oracle, with the bounds of test_random_workloads_every_row."""
+    w, ns, out_f32, precise, outliers, desc = random_medium_case(seed)
+    print("random medium %d: %s" % (seed, desc), flush=True)
+    kw = {}
+    if not precise:
+        kw["extra_abs"] = p_rounding_bound(w, precise=False)
+        if outliers:
+            kw["mean_rel_max"] = 2.0 ** -8 + 2.0 ** -11
+    full_check(w, num_splits=ns, out_f32=out_f32, label="random medium %d" % seed,
+               flags=PRECISE if precise else 0, **kw)
